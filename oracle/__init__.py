@@ -1,0 +1,188 @@
+"""Oracle for exact attention (fp64, CPU).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
+leg of the benchmark may import this package; the library and its Python
+binding never do. It shares no code with the HIP kernels.
+
+Contents
+  attention()        fp64 attention by its definition, in C with OpenMP
+                     (attention_f64.c), for any shape
+  brute_force()      the same definition as plain Python loops with math.fsum,
+                     for tiny shapes; it cross-checks the C routine
+  combine_splits()   the third Flash-Decoding step in fp64
+  widen()            exact decode of fp16 / bf16 bit patterns to float64
+
+Sources, all restated rather than copied:
+  "flash-attention-v100" README, How to use FlashAttention: the definition
+  softmax(Q K^T * softmax_scale) V, default scale 1/sqrt(headdim), the GQA head
+  map, the bottom-right causal mask with all-zero output for a fully masked
+  row, the sliding-window band and cache_seqlens;
+  "flash attention-2 github" search page, Flash-Decoding description: split the
+  keys/values into chunks, attend to each chunk, write a log-sum-exp per row and
+  chunk, then combine.
+
+Where the pages are silent the oracle takes these readings: the LSE is the
+natural log-sum-exp of the scaled and masked scores; a row with no visible key
+has LSE = -inf; the combine weights chunk s by exp(LSE_s - LSE) with
+LSE = log(sum_s exp(LSE_s)), and returns O = 0, LSE = -inf when every chunk is
+empty.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attention_f64.c")
+_LIB = os.path.join(_HERE, "liboracle_f64.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (plain IEEE double arithmetic, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+                               "-shared", "-fPIC", "-Wall", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        L = ctypes.c_long
+        lib.oracle_attention_f64.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L, L, ctypes.c_int,
+                                             L, L, ctypes.POINTER(ctypes.c_int), L, L,
+                                             ctypes.c_double]
+        lib.oracle_attention_f64.restype = ctypes.c_int
+        lib.oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 values of 16-bit storage patterns (IEEE binary16 or bfloat16)."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    if dtype == "f16":
+        return bits.view(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def attention(q, k, v, causal=False, scale=None, window=(-1, -1), seqlens_k=None,
+              key_range=None):
+    """fp64 attention. q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d] (float64) -> (o [B,Nq,Hq,d], lse [B,Hq,Nq])."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    B, Nq, Hq, d = q.shape
+    Bk, Nk, Hkv, dk = k.shape
+    if k.shape != v.shape or Bk != B or dk != d:
+        raise ValueError("shape mismatch")
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = np.zeros((B, Nq, Hq, d), np.float64)
+    lse = np.zeros((B, Hq, Nq), np.float64)
+    kb, ke = (0, Nk) if key_range is None else key_range
+    sl = None
+    if seqlens_k is not None:
+        sl = np.ascontiguousarray(seqlens_k, dtype=np.int32)
+        if sl.shape != (B,):
+            raise ValueError("seqlens_k must have shape (B,)")
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = _load().oracle_attention_f64(
+        q.ctypes.data_as(dp), k.ctypes.data_as(dp), v.ctypes.data_as(dp),
+        o.ctypes.data_as(dp), lse.ctypes.data_as(dp), B, Nq, Nk, Hq, Hkv, d, int(bool(causal)),
+        int(window[0]), int(window[1]),
+        None if sl is None else sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int)),
+        int(kb), int(ke), float(scale))
+    if rc != 0:
+        raise RuntimeError(f"oracle failed with code {rc}")
+    return o, lse
+
+
+def attention_bits(qb, kb, vb, dtype, **kw):
+    """Oracle on 16-bit input patterns, widened exactly to float64."""
+    return attention(widen(qb, dtype), widen(kb, dtype), widen(vb, dtype), **kw)
+
+
+def visible(i, j, Nq, Nk, causal, window=(-1, -1)):
+    """Mask predicate, written out for the brute force: may query i see key j?"""
+    diag = i + Nk - Nq
+    if j < 0 or j >= Nk:
+        return False
+    if causal and j > diag:
+        return False
+    if window[0] >= 0 and j < diag - window[0]:
+        return False
+    if window[1] >= 0 and j > diag + window[1]:
+        return False
+    return True
+
+
+def brute_force(q, k, v, causal=False, scale=None, window=(-1, -1), return_probs=False):
+    """Pure-Python loops over nested lists/arrays; for tiny shapes only."""
+    B, Nq, Hq, d = np.shape(q)
+    _, Nk, Hkv, _ = np.shape(k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    group = Hq // Hkv
+    o = np.zeros((B, Nq, Hq, d))
+    lse = np.zeros((B, Hq, Nq))
+    probs = np.zeros((B, Hq, Nq, Nk))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            for i in range(Nq):
+                keys = [j for j in range(Nk) if visible(i, j, Nq, Nk, causal, window)]
+                if not keys:
+                    lse[b, h, i] = -math.inf
+                    continue
+                s = {j: scale * math.fsum(float(q[b][i][h][c]) * float(k[b][j][g][c])
+                                          for c in range(d)) for j in keys}
+                m = max(s.values())
+                e = {j: math.exp(s[j] - m) for j in keys}
+                den = math.fsum(e.values())
+                for j in keys:
+                    probs[b, h, i, j] = e[j] / den
+                for c in range(d):
+                    o[b, i, h, c] = math.fsum(e[j] * float(v[b][j][g][c]) for j in keys) / den
+                lse[b, h, i] = m + math.log(den)
+    if return_probs:
+        return o, lse, probs
+    return o, lse
+
+
+def combine_splits(o_parts, lse_parts):
+    """Merge per-chunk results: o_parts [S,B,Nq,Hq,d], lse_parts [S,B,Hq,Nq] -> (o, lse).
+
+    LSE = log(sum_s exp(LSE_s)); O = sum_s exp(LSE_s - LSE) * O_s. Chunks with
+    LSE_s = -inf weigh nothing; if all are -inf the row is O = 0, LSE = -inf.
+    """
+    o_parts = np.asarray(o_parts, np.float64)
+    lse_parts = np.asarray(lse_parts, np.float64)
+    mx = np.max(lse_parts, axis=0)
+    finite = np.isfinite(mx)
+    base = np.where(finite, mx, 0.0)
+    w = np.exp(lse_parts - base[None])                     # [S,B,Hq,Nq]
+    tot = np.sum(w, axis=0)
+    lse = np.where(finite, base + np.log(np.where(finite, tot, 1.0)), -np.inf)
+    wn = np.where(finite[None], w / np.where(finite, tot, 1.0)[None], 0.0)
+    o = np.einsum("sbhi,sbihc->bihc", wn, o_parts)
+    return o, lse
