@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one forward pass over the pages' headline workload
+[B=16, N=1024, H=32, d=128] fp16, non-causal (inputs resident in HBM). The line
+also carries the split-KV decode step (split + combine kernels) at
+B=8, Nq=1, Nk=8192, Hq=32, Hkv=8, d=128 bf16 with 16 chunks, and the forward at
+N=4096, each timed the same way. Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_F16 = 2500.0     # TFLOP/s, MI355X dense fp16/bf16 (published)
+PEAK_HBM = 8000.0          # GB/s, MI355X HBM3E (published)
+METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) & % MFMA peak; split-KV decode µs/step"
+PAGES_HEADLINE_TFLOPS_4X = 51.68   # RTX 3080 official FA2 at [16,1024,32,128], 5.32 ms (pages' table, x2)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_headline_traffic.json")
+KERNEL_SOURCES = ("fa_fwd_kernel.h", "fa_device.h", "fa_launch.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_tiled_attention_21_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None if the
+    kernel sources changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_steps(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps   # ms per step
+
+
+def upload(w, torch):
+    """Seeded 16-bit inputs of workload w, copied to the GPU before any timing."""
+    import numpy as np
+    dt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+    return tuple(torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda:0").view(dt)
+                 for x in w.inputs())
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The oracle, as it stands, on the host cores: b = 0 and the first n heads of the
+    workload (all query rows, all keys), n grown until the run takes ~budget_s."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    threads = oracle.num_threads()
+    qb, kb, vb = w.inputs(batches=[0])
+    q, k, v = (oracle.widen(x, w.dtype) for x in (qb, kb, vb))
+    n, took = 1, 0.0
+    while True:
+        t0 = time.perf_counter()
+        oracle.attention(q[:, :, :n], k[:, :, :n], v[:, :, :n], causal=w.causal, scale=w.scale)
+        took = time.perf_counter() - t0
+        if took >= budget_s / 3 or n >= w.Hq:
+            break
+        n = min(w.Hq, max(n * 2, int(n * budget_s / 3 / max(took, 1e-3))))
+    flops = 4.0 * n * w.pairs() * w.d
+    return {"value": flops / took / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.name}: batch 0, heads 0..{n - 1}, all {w.Nq} query rows x {w.Nk} keys, fp64 "
+                      f"({took:.1f} s)", "seconds": took}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--only", choices=["fwd", "decode", "all"], default="all")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import synthetic
+    from exact_tiled_attention_21_amd import attention, decode, decode_workspace_bytes
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    dev = torch.device("cuda:0")
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "data": "synthetic"}
+
+    # ---- forward, headline workload (the line's value)
+    w = synthetic.WORKLOADS["headline_f16_1024"]
+    if args.only in ("fwd", "all"):
+        q, k, v = upload(w, torch)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+        ms = time_steps(lambda i=0: attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse),
+                        args.steps, args.warmup, torch)
+        tflops = w.flops() / (ms * 1e-3) / 1e12
+        traffic = measured_traffic()
+        result.update({
+            "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 4),
+            "vs_baseline": round(tflops / PAGES_HEADLINE_TFLOPS_4X, 2), "dtype": "f16",
+            "config": {"workload": w.name, "B": w.B, "Nq": w.Nq, "Nk": w.Nk, "Hq": w.Hq, "Hkv": w.Hkv,
+                       "d": w.d, "causal": w.causal},
+            "tflops_pages_convention": round(tflops / 2, 2),
+            "mfma_peak_frac": round(tflops / PEAK_MFMA_F16, 4),
+            "roofline": {"bound": "mfma", "kernel": "fa_fwd_kernel<128,f16,noncausal>",
+                         "achieved": round(tflops, 2), "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
+                         "frac": round(tflops / PEAK_MFMA_F16, 4),
+                         "traffic": traffic},
+        })
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+
+        # forward at N = 4096 (the 50%-of-peak target shape)
+        w4 = synthetic.WORKLOADS["long_f16_4096_full"]
+        q, k, v = upload(w4, torch)
+        o = torch.empty_like(q)
+        ms4 = time_steps(lambda i=0: attention(q, k, v, scale=w4.scale, out=o), max(5, args.steps // 5),
+                         max(2, args.warmup // 5), torch)
+        t4 = w4.flops() / (ms4 * 1e-3) / 1e12
+        result["fwd_4096"] = {"workload": w4.name, "ms": round(ms4, 4), "tflops": round(t4, 2),
+                              "tflops_pages_convention": round(t4 / 2, 2),
+                              "mfma_peak_frac": round(t4 / PEAK_MFMA_F16, 4)}
+        del q, k, v, o
+        torch.cuda.empty_cache()
+
+    # ---- split-KV decode, rotating over KV sets larger than the 256 MB infinity cache
+    if args.only in ("decode", "all"):
+        wd = synthetic.WORKLOADS["decode_bf16_nq1"]
+        sets = []
+        for r in range(4):
+            import dataclasses
+            wr = dataclasses.replace(wd, wid=wd.wid + 1000 * r)
+            sets.append(upload(wr, torch))
+        ws = torch.empty(decode_workspace_bytes(wd.B, wd.Nq, wd.Hq, wd.d, wd.num_splits), dtype=torch.uint8,
+                         device=dev)
+        o = torch.empty_like(sets[0][0])
+        lse = torch.empty((wd.B, wd.Hq, wd.Nq), dtype=torch.float32, device=dev)
+
+        def dstep(i=0):
+            qq, kk, vv = sets[i % len(sets)]
+            decode(qq, kk, vv, num_splits=wd.num_splits, scale=wd.scale, workspace=ws, out=o, lse=lse)
+
+        msd = time_steps(dstep, max(args.steps, 100), args.warmup, torch)
+        kv_bytes = 2 * wd.B * wd.Nk * wd.Hkv * wd.d * 2
+        result["decode"] = {"workload": wd.name, "us_per_step": round(msd * 1e3, 2),
+                            "kv_GBps": round(kv_bytes / (msd * 1e-3) / 1e9, 1),
+                            "hbm_peak_frac": round(kv_bytes / (msd * 1e-3) / 1e9 / PEAK_HBM, 4),
+                            "roofline_us": round(kv_bytes / (PEAK_HBM * 1e9) * 1e6, 2),
+                            "kv_sets_rotated": len(sets)}
+        if "value" not in result:
+            result.update({"value": round(msd * 1e3, 2), "unit": "us/step", "higher_is_better": False,
+                           "ms_per_step": round(msd, 5), "vs_baseline": None, "dtype": "bf16",
+                           "config": {"workload": wd.name}})
+        del sets, ws, o, lse
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,105 @@
+"""Exact tiled attention for MI355X: the Python face of libfa (include/fa.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libfa.so. torch supplies device memory and the current stream.
+
+  attention(q, k, v, causal=False, scale=None) -> (o, lse)
+  decode(q, k_cache, v_cache, num_splits=16, scale=None, causal=False) -> (o, lse)
+
+Tensors are [batch, seq_len, heads, head_dim], fp16 or bf16, contiguous, on a
+ROCm device; lse is float32 [batch, heads, seq_len_q]. The default scale is
+1/sqrt(head_dim) ("flash-attention-v100" README, How to use FlashAttention).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+from ._lib import FA_BF16, FA_F16, FA_MAX_SPLITS, FaError, load, status_str  # noqa: F401
+
+__all__ = ["attention", "decode", "decode_workspace_bytes", "FaError", "load"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return FA_F16
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"dtype must be float16 or bfloat16, got {t.dtype}")
+
+
+def _check(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [batch, seq_len, heads, head_dim]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    if q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3]:
+        raise ValueError("batch and head_dim of q and k must match")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """Exact attention forward: softmax(scale * q k^T [+ causal mask]) v, plus per-row LSE."""
+    torch = _torch()
+    _check(q, k, v)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    with torch.cuda.device(q.device):
+        st = load().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(),
+                           B, Nq, Nk, Hq, Hkv, d, int(bool(causal)), float(scale), _dtype_code(q),
+                           _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_fwd")
+    return o, lse_t
+
+
+def decode_workspace_bytes(B: int, Nq: int, Hq: int, d: int, num_splits: int) -> int:
+    return int(load().fa_decode_workspace_bytes(B, Nq, Hq, d, num_splits))
+
+
+def decode(q, k_cache, v_cache, num_splits: int = 16, scale: float | None = None,
+           causal: bool = False, workspace=None, out=None, lse=None):
+    """Split-KV (Flash-Decoding) attention of a short query block over a KV cache."""
+    torch = _torch()
+    _check(q, k_cache, v_cache)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_bytes(B, Nq, Hq, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    with torch.cuda.device(q.device):
+        st = load().fa_decode_splitkv(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(),
+                                      lse_t.data_ptr(), B, Nq, Nk, Hq, Hkv, d, int(num_splits),
+                                      int(bool(causal)), float(scale), _dtype_code(q),
+                                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                      _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_decode_splitkv")
+    return o, lse_t

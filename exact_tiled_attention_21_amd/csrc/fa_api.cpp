@@ -1,0 +1,154 @@
+// C ABI of libfa: argument validation and dispatch. Every check runs before
+// the first HIP call, so invalid calls return a status without a GPU.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace fa {
+hipError_t launch_fwd_d32(const FwdArgs&, bool, bool, hipStream_t);
+hipError_t launch_fwd_d64(const FwdArgs&, bool, bool, hipStream_t);
+hipError_t launch_fwd_d96(const FwdArgs&, bool, bool, hipStream_t);
+hipError_t launch_fwd_d128(const FwdArgs&, bool, bool, hipStream_t);
+hipError_t launch_fwd_d192(const FwdArgs&, bool, bool, hipStream_t);
+hipError_t launch_fwd_d256(const FwdArgs&, bool, bool, hipStream_t);
+hipError_t launch_decode_d32(const DecodeArgs&, bool, bool, hipStream_t);
+hipError_t launch_decode_d64(const DecodeArgs&, bool, bool, hipStream_t);
+hipError_t launch_decode_d96(const DecodeArgs&, bool, bool, hipStream_t);
+hipError_t launch_decode_d128(const DecodeArgs&, bool, bool, hipStream_t);
+hipError_t launch_decode_d192(const DecodeArgs&, bool, bool, hipStream_t);
+hipError_t launch_decode_d256(const DecodeArgs&, bool, bool, hipStream_t);
+
+hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool causal, hipStream_t s) {
+  switch (d) {
+    case 32: return launch_fwd_d32(a, bf16, causal, s);
+    case 64: return launch_fwd_d64(a, bf16, causal, s);
+    case 96: return launch_fwd_d96(a, bf16, causal, s);
+    case 128: return launch_fwd_d128(a, bf16, causal, s);
+    case 192: return launch_fwd_d192(a, bf16, causal, s);
+    case 256: return launch_fwd_d256(a, bf16, causal, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, bool causal, hipStream_t s) {
+  switch (d) {
+    case 32: return launch_decode_d32(a, bf16, causal, s);
+    case 64: return launch_decode_d64(a, bf16, causal, s);
+    case 96: return launch_decode_d96(a, bf16, causal, s);
+    case 128: return launch_decode_d128(a, bf16, causal, s);
+    case 192: return launch_decode_d192(a, bf16, causal, s);
+    case 256: return launch_decode_d256(a, bf16, causal, s);
+  }
+  return hipErrorInvalidValue;
+}
+}  // namespace fa
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;  // per tensor, keeps 64-bit offsets far from overflow
+
+bool head_dim_ok(int d) {
+  return d == 32 || d == 64 || d == 96 || d == 128 || d == 192 || d == 256;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+fa_status check_common(const void* q, const void* k, const void* v, void* o, const float* lse,
+                       int B, int Nq, int Nk, int Hq, int Hkv, int d, float scale, fa_dtype dtype) {
+  if (!q || !k || !v || !o) return FA_ERR_NULLPTR;
+  if (B < 1 || Nq < 1 || Nk < 1 || Hq < 1 || Hkv < 1) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_HEADS;
+  if (!head_dim_ok(d)) return FA_ERR_HEADDIM;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  const int64_t qe = int64_t(B) * Nq * Hq * d, ke = int64_t(B) * Nk * Hkv * d;
+  if (qe > kMaxElems || ke > kMaxElems) return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+size_t pad256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int decode_chunk(int Nk, int splits) {
+  const int per = (Nk + splits - 1) / splits;
+  return (per + 31) / 32 * 32;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale,
+                 fa_dtype dtype, void* stream) {
+  fa_status st = check_common(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, scale, dtype);
+  if (st != FA_OK) return st;
+  fa::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.Nq = Nq; a.Nk = Nk; a.Hq = Hq; a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  a.n_qtiles = (Nq + fa::kFwdRows - 1) / fa::kFwdRows;
+  a.sl2 = scale * 1.4426950408889634f;
+  const int64_t blocks = int64_t(a.n_qtiles) * Hq * B;
+  if (blocks > 0x7fffffff) return FA_ERR_SHAPE;
+  hipError_t e = fa::launch_fwd(a, d, dtype == FA_BF16, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_decode_workspace_bytes(int B, int Nq, int Hq, int d, int num_splits) {
+  if (B < 1 || Nq < 1 || Hq < 1 || !head_dim_ok(d) || num_splits < 1 || num_splits > FA_MAX_SPLITS)
+    return 0;
+  const size_t rows = size_t(num_splits) * B * Hq * Nq;
+  return pad256(rows * d * sizeof(float)) + pad256(rows * sizeof(float));
+}
+
+fa_status fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache, void* o,
+                            float* lse, int B, int Nq, int Nk, int Hq, int Hkv, int d,
+                            int num_splits, int causal, float scale, fa_dtype dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  fa_status st = check_common(q, k_cache, v_cache, o, lse, B, Nq, Nk, Hq, Hkv, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!workspace) return FA_ERR_NULLPTR;
+  if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
+  const size_t need = fa_decode_workspace_bytes(B, Nq, Hq, d, num_splits);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  const int group = Hq / Hkv;
+  const int64_t row_blocks = (int64_t(group) * Nq + 31) / 32;
+  if (row_blocks * Hkv > 65535 || B > 65535) return FA_ERR_SHAPE;  // grid y / z limits
+  fa::DecodeArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse;
+  const size_t rows = size_t(num_splits) * B * Hq * Nq;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pad256(rows * d * sizeof(float)));
+  a.B = B; a.Nq = Nq; a.Nk = Nk; a.Hq = Hq; a.Hkv = Hkv;
+  a.group = group;
+  a.splits = num_splits;
+  a.chunk = decode_chunk(Nk, num_splits);
+  a.row_blocks = static_cast<int>(row_blocks);
+  a.sl2 = scale * 1.4426950408889634f;
+  hipError_t e = fa::launch_decode(a, d, dtype == FA_BF16, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+const char* fa_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULLPTR: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "a size is < 1 or too large";
+    case FA_ERR_HEADS: return "Hq is not a multiple of Hkv";
+    case FA_ERR_HEADDIM: return "head dim must be one of 32, 64, 96, 128, 192, 256";
+    case FA_ERR_DTYPE: return "dtype must be FA_F16 or FA_BF16";
+    case FA_ERR_SPLITS: return "num_splits must be in 1..FA_MAX_SPLITS";
+    case FA_ERR_WORKSPACE: return "workspace smaller than fa_decode_workspace_bytes()";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case FA_ERR_SCALE: return "scale is not finite";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

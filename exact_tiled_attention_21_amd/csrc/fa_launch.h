@@ -1,0 +1,43 @@
+// Host-side launch interface between the C ABI (fa_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;      // may be null
+  int B, Nq, Nk, Hq, Hkv;
+  int group;       // Hq / Hkv
+  int n_qtiles;    // ceil(Nq / rows per workgroup)
+  float sl2;       // scale * log2(e)
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;      // may be null
+  float* part_o;   // [S][B][Hq][Nq][d] float32
+  float* part_lse; // [S][B][Hq][Nq] float32, log2 domain
+  int B, Nq, Nk, Hq, Hkv;
+  int group;       // Hq / Hkv
+  int splits;      // S
+  int chunk;       // keys per split, a multiple of 32
+  int row_blocks;  // ceil(group * Nq / 32)
+  float sl2;       // scale * log2(e)
+};
+
+// Rows of queries one forward workgroup covers.
+constexpr int kFwdRows = 128;
+
+hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,119 @@
+/*
+ * fa.h -- C ABI of libfa: exact tiled attention on MI355X (gfx950).
+ *
+ * Two operations:
+ *   fa_fwd             the exact attention forward pass, computed tile by tile
+ *                      with an online softmax so the Nq x Nk score matrix never
+ *                      reaches device memory;
+ *   fa_decode_splitkv  the same result for short query blocks, with the keys
+ *                      split into chunks that are processed in parallel and a
+ *                      second kernel that merges the per-chunk results.
+ *
+ * Definition ("flash-attention-v100" README, How to use FlashAttention):
+ *   O = softmax(scale * Q K^T) V, row by row, with
+ *   - grouped-query heads: query head h reads key/value head h / (Hq / Hkv);
+ *     Hq must be a multiple of Hkv (flash_attn_func docstring);
+ *   - causal = 1: query i sees key j iff j <= i + Nk - Nq, the mask aligned to
+ *     the bottom-right corner (Changelog 2.1; flash_attn_with_kvcache
+ *     docstring); a row that sees no key gets O = 0.
+ * Flash-Decoding ("flash attention-2 github" search page; "flash-attention-v100"
+ * README, Changelog 2.2): split the keys into chunks, attend to each chunk in
+ * parallel while writing one log-sum-exp per row and chunk, then combine.
+ *
+ * Layouts (row-major, head_dim fastest; "ampere_flash_attention_from_scratch"
+ * README, Performance Test header [batch_size, seq_len, num_heads, head_dim]):
+ *   q, o      [B][Nq][Hq][d]   dtype
+ *   k, v      [B][Nk][Hkv][d]  dtype  (for decode: the KV cache)
+ *   lse       [B][Hq][Nq]      float32, natural log of sum_j exp(scale*q.k_j)
+ *                              over the visible keys; -inf for a row that sees
+ *                              no key. May be NULL (then not written).
+ *
+ * Ownership and execution: every pointer is a device pointer owned by the
+ * caller. The library never allocates, frees or synchronises; it enqueues
+ * kernels on `stream` (a hipStream_t; NULL is the default stream) and returns.
+ * Calls are stateless and reentrant. Outputs are fully overwritten.
+ *
+ * Errors: arguments are validated before any HIP call, so a bad call returns a
+ * status without touching the GPU. FA_ERR_LAUNCH reports a failed launch;
+ * faults during execution surface at the caller's next synchronisation.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULLPTR = 1,   /* q, k, v or o is NULL (or workspace for decode)   */
+  FA_ERR_SHAPE = 2,     /* B, Nq, Nk, Hq or Hkv < 1, or a size overflows    */
+  FA_ERR_HEADS = 3,     /* Hq is not a multiple of Hkv                      */
+  FA_ERR_HEADDIM = 4,   /* d not in {32, 64, 96, 128, 192, 256}             */
+  FA_ERR_DTYPE = 5,     /* dtype not FA_F16 or FA_BF16                      */
+  FA_ERR_SPLITS = 6,    /* num_splits < 1 or > FA_MAX_SPLITS                */
+  FA_ERR_WORKSPACE = 7, /* workspace_bytes < fa_decode_workspace_bytes(...) */
+  FA_ERR_LAUNCH = 8,    /* the HIP runtime rejected a kernel launch         */
+  FA_ERR_ALIGN = 9,     /* a tensor pointer is not 16-byte aligned          */
+  FA_ERR_SCALE = 10     /* scale is not a finite number                     */
+} fa_status;
+
+typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
+
+#define FA_MAX_SPLITS 256
+
+/*
+ * Attention forward pass.
+ *   q, k, v, o : device tensors in the layouts above, `dtype` elements,
+ *                16-byte aligned. o must not overlap q, k or v.
+ *   lse        : device float32 [B][Hq][Nq] or NULL.
+ *   B, Nq, Nk, Hq, Hkv, d : sizes; Nq != Nk is allowed (with causal = 1 the
+ *                mask is bottom-right aligned).
+ *   causal     : 0 or 1 (any non-zero value means 1).
+ *   scale      : multiplies Q K^T before the softmax, used exactly as passed
+ *                (the pages' default is 1/sqrt(d); the Python layer applies it).
+ *   dtype      : FA_F16 or FA_BF16; accumulation is float32, P is rounded to
+ *                dtype before the P V product, O is rounded to nearest even.
+ * Returns FA_OK or an error status; on error nothing is enqueued.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale,
+                 fa_dtype dtype, void* stream);
+
+/*
+ * Bytes of device workspace fa_decode_splitkv needs: float32 partial outputs
+ * [num_splits][B][Hq][Nq][d] followed by float32 partial LSEs
+ * [num_splits][B][Hq][Nq], each part padded to 256 bytes. Returns 0 for
+ * invalid sizes.
+ */
+size_t fa_decode_workspace_bytes(int B, int Nq, int Hq, int d, int num_splits);
+
+/*
+ * Split-KV attention (Flash-Decoding) over a contiguous KV cache.
+ *   q, o       : [B][Nq][Hq][d]; k_cache, v_cache: [B][Nk][Hkv][d]; all `dtype`.
+ *   lse        : float32 [B][Hq][Nq] or NULL.
+ *   num_splits : number of key chunks S, 1..FA_MAX_SPLITS. Chunk s covers keys
+ *                [s*C, min(Nk, (s+1)*C)) with C = ceil(Nk/S) rounded up to a
+ *                multiple of 32; chunks past Nk are empty and weigh nothing.
+ *   causal     : as in fa_fwd (bottom-right aligned against Nk).
+ *   workspace  : caller-owned device buffer of at least
+ *                fa_decode_workspace_bytes(B, Nq, Hq, d, num_splits) bytes,
+ *                16-byte aligned; its contents on entry do not matter.
+ * Two kernels are enqueued on `stream`: the per-chunk pass, then the merge.
+ * The result equals fa_fwd's on the same inputs up to float32 rounding.
+ */
+fa_status fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache, void* o,
+                            float* lse, int B, int Nq, int Nk, int Hq, int Hkv, int d,
+                            int num_splits, int causal, float scale, fa_dtype dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* fa_status_str(fa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -47,19 +47,36 @@ def to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
+def _slice_bits(workload_id, tensor_id, b, rest, dtype, mult):
+    rng = np.random.default_rng([int(workload_id), int(tensor_id), int(b)])
+    x = rng.standard_normal(rest, dtype=np.float32)
+    if mult != 1.0:
+        x *= np.float32(mult)
+    return to_bits(x, dtype)
+
+
 def normal_bits(workload_id: int, tensor_id: int, shape, dtype: str, mult: float = 1.0,
-                batches=None) -> np.ndarray:
-    """16-bit patterns of N(0,1)*mult, shape [B, N, H, d]; ``batches`` picks a subset of b."""
+                batches=None, threads: int = 8) -> np.ndarray:
+    """16-bit patterns of N(0,1)*mult, shape [B, N, H, d]; ``batches`` picks a subset of b.
+
+    Each batch slice has its own generator, seeded [workload_id, tensor_id, b],
+    so the result does not depend on ``batches`` or on the thread count.
+    """
     B = int(shape[0])
     rest = tuple(int(s) for s in shape[1:])
-    bs = range(B) if batches is None else list(batches)
+    bs = list(range(B)) if batches is None else [int(b) for b in batches]
     out = np.empty((len(bs),) + rest, dtype=np.uint16)
-    for n, b in enumerate(bs):
-        rng = np.random.default_rng([int(workload_id), int(tensor_id), int(b)])
-        x = rng.standard_normal(rest, dtype=np.float32)
-        if mult != 1.0:
-            x = x * np.float32(mult)
-        out[n] = to_bits(x, dtype)
+
+    def fill(n):
+        out[n] = _slice_bits(workload_id, tensor_id, bs[n], rest, dtype, mult)
+
+    if threads > 1 and len(bs) > 1 and out.nbytes > (1 << 22):
+        import concurrent.futures as cf
+        with cf.ThreadPoolExecutor(max_workers=min(threads, len(bs))) as ex:
+            list(ex.map(fill, range(len(bs))))
+    else:
+        for n in range(len(bs)):
+            fill(n)
     return out
 
 

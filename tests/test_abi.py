@@ -1,0 +1,111 @@
+"""C ABI checks that need no GPU: the library loads, exports what include/fa.h
+declares, and rejects every invalid call before any HIP call.
+
+Only invalid calls are made here: fake device addresses never pass validation,
+so nothing is ever launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_tiled_attention_21_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+MIS = 0x10008           # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(11):
+        s = lib.fa_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert lib.fa_status_str(99).decode() == "unknown status"
+
+
+def fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Nq=8, Nk=8, Hq=2, Hkv=1, d=64,
+        causal=0, scale=0.125, dtype=0):
+    return lib.fa_fwd(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
+    (dict(B=0), 2), (dict(Nq=0), 2), (dict(Nk=-1), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2),
+    (dict(B=1 << 20, Nq=1 << 20, Hq=64, d=256), 2),
+    (dict(Hq=3, Hkv=2), 3),
+    (dict(d=48), 4), (dict(d=16), 4), (dict(d=512), 4), (dict(d=0), 4),
+    (dict(dtype=2), 5), (dict(dtype=-1), 5),
+    (dict(scale=float("inf")), 10), (dict(scale=float("nan")), 10),
+    (dict(q=MIS), 9), (dict(o=MIS), 9), (dict(lse=FAKE + 2), 9),
+])
+def test_fwd_rejects_invalid_arguments(lib, kw, status):
+    assert fwd(lib, **kw) == status
+
+
+def test_fwd_checks_nullptr_before_shape(lib):
+    assert fwd(lib, q=None, B=0) == 1
+
+
+def test_workspace_size(lib):
+    ws = lib.fa_decode_workspace_bytes
+    # [S][B][Hq][Nq][d] fp32 partial outputs, then [S][B][Hq][Nq] fp32 LSEs, each padded to 256 B
+    rows = 16 * 8 * 32 * 1
+    assert ws(8, 1, 32, 128, 16) == rows * 128 * 4 + ((rows * 4 + 255) // 256) * 256
+    assert ws(8, 1, 32, 128, 0) == 0
+    assert ws(8, 1, 32, 100, 4) == 0
+    assert ws(0, 1, 32, 128, 4) == 0
+    assert ws(1, 1, 1, 32, _lib.FA_MAX_SPLITS + 1) == 0
+
+
+def dec(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, Nq=1, Nk=64, Hq=4, Hkv=2, d=128, S=4,
+        causal=0, scale=0.1, dtype=1, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = lib.fa_decode_workspace_bytes(B, Nq, Hq, d, S) if S >= 1 else 0
+    return lib.fa_decode_splitkv(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, S, causal, scale, dtype,
+                                 ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(ws=None), 1), (dict(o=None), 1),
+    (dict(Nk=0), 2), (dict(Hq=5, Hkv=2), 3), (dict(d=80), 4), (dict(dtype=7), 5),
+    (dict(S=0), 6), (dict(S=_lib.FA_MAX_SPLITS + 1), 6),
+    (dict(wsb=16), 7), (dict(ws=MIS), 9), (dict(k=MIS), 9), (dict(scale=float("-inf")), 10),
+])
+def test_decode_rejects_invalid_arguments(lib, kw, status):
+    assert dec(lib, **kw) == status
+
+
+def test_python_layer_fails_loudly_without_library(tmp_path):
+    with pytest.raises(FileNotFoundError):
+        _lib.load(str(tmp_path / "libfa.so"))
+
+
+def test_no_oracle_on_product_path():
+    pkg = os.path.join(ROOT, "exact_tiled_attention_21_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "attention_f64" not in text, f

@@ -1,0 +1,131 @@
+"""GPU parity of fa_fwd against the fp64 oracle, through the C ABI.
+
+Whole tensors at small sizes (several tiles, ragged tails, every head dim,
+both dtypes, Nq != Nk, fully masked rows) and at the pages' headline shape
+for one batch element; sampled rows (all heads, first and last batch) at the
+long-sequence and GQA sizes, in the launch configuration the benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import _compare as cmp
+import oracle
+import synthetic
+from gpu_util import oracle_rows, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+from exact_tiled_attention_21_amd import attention  # noqa: E402
+
+HEAD_DIMS = (32, 64, 96, 128, 192, 256)
+
+
+def run_full(wid, B, Nq, Nk, Hq, Hkv, d, dtype, causal, qk_mult=1.0, scale=None):
+    sq, sk = (B, Nq, Hq, d), (B, Nk, Hkv, d)
+    qb = synthetic.normal_bits(wid, 0, sq, dtype, qk_mult)
+    kb = synthetic.normal_bits(wid, 1, sk, dtype, qk_mult)
+    vb = synthetic.normal_bits(wid, 2, sk, dtype)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    print(f"[fwd] wid={wid} B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} {dtype} causal={causal}", flush=True)
+    o, lse = attention(to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype), causal=causal, scale=scale)
+    o_ref, lse_ref = oracle.attention_bits(qb, kb, vb, dtype, causal=causal, scale=scale)
+    what = f"B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} {dtype} causal={causal}"
+    stats = cmp.check_o(to_np(o), o_ref, dtype, what)
+    cmp.check_lse(to_np(lse), lse_ref, what)
+    return stats
+
+
+def test_tiny_workload():
+    w = synthetic.WORKLOADS["tiny_f16_128"]
+    run_full(w.wid, w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.d, w.dtype, w.causal)
+
+
+EDGE = [
+    (1, 9, 9, 12, 12, 64, "f16", False),      # GPT-2 sized example: seq 9, 12 heads, d 64
+    (1, 9, 9, 12, 12, 64, "bf16", True),
+    (2, 127, 129, 4, 2, 128, "bf16", True),
+    (2, 129, 127, 4, 1, 128, "f16", True),    # Nq > Nk: first rows see no key
+    (1, 300, 37, 2, 2, 64, "bf16", True),     # most rows fully masked
+    (1, 37, 300, 2, 2, 64, "f16", True),
+    (1, 1, 1, 1, 1, 32, "f16", False),
+    (1, 1, 513, 2, 1, 128, "bf16", False),
+    (1, 513, 1, 2, 1, 128, "bf16", False),
+    (1, 256, 1000, 8, 8, 128, "f16", False),
+    (3, 250, 250, 6, 6, 96, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: "x".join(map(str, c)))
+def test_edge_shapes(case):
+    run_full(100 + EDGE.index(case), *case)
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dims(d, dtype, causal):
+    wid = 200 + HEAD_DIMS.index(d) * 4 + (dtype == "bf16") * 2 + int(causal)
+    run_full(wid, 2, 200, 333, 6, 2, d, dtype, causal)
+
+
+def test_scale_is_used_as_passed():
+    run_full(300, 1, 130, 130, 2, 2, 64, "f16", False, scale=0.37)
+    run_full(301, 1, 130, 130, 2, 2, 64, "bf16", True, scale=0.0)
+
+
+def run_sampled(w, seed):
+    """Whole workload on the GPU; oracle on sampled rows of b = 0 and b = B-1."""
+    q, k, v = w.inputs()
+    print(f"[fwd sampled] {w.name}", flush=True)
+    o, lse = attention(to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, w.dtype), causal=w.causal, scale=w.scale)
+    o_np = o.float().cpu().numpy()
+    lse_np = lse.cpu().numpy()
+    del o, lse
+    rng = np.random.default_rng(seed)
+    rows = cmp.sample_rows(w.Nq, rng)
+    worst = {}
+    for b in sorted({0, w.B - 1}):
+        o_ref, lse_ref = oracle_rows(q[b:b + 1], k[b:b + 1], v[b:b + 1], w.dtype, rows, w.causal, w.scale)
+        what = f"{w.name} b={b}"
+        st = cmp.check_o(o_np[b:b + 1, rows].astype(np.float64), o_ref, w.dtype, what)
+        cmp.check_lse(lse_np[b:b + 1][:, :, rows].astype(np.float64), lse_ref, what)
+        # secondary rule: within 2x the error of a plain float32 implementation (+1 ulp)
+        qf, kf, vf = (oracle.widen(x[b], w.dtype) for x in (q, k, v))
+        for h in (0, w.Hq - 1):
+            g = h // (w.Hq // w.Hkv)
+            base = cmp.emulate_rows(qf[:, h], kf[:, g], vf[:, g], rows, h, w.causal, w.scale, w.dtype, w.Nq)
+            ref = o_ref[0, :, h]
+            e_gpu = np.abs(o_np[b, rows, h] - ref).max()
+            e_base = np.abs(base - ref).max()
+            slack = cmp.ulp(np.abs(ref).max(), w.dtype)
+            assert e_gpu <= 2 * e_base + slack, f"{what} h={h}: {e_gpu:.3g} > 2*{e_base:.3g} + {slack:.3g}"
+        worst = {k2: max(worst.get(k2, 0), v2) for k2, v2 in st.items()}
+    print(f"[fwd sampled] {w.name}: {cmp.fmt(worst)}", flush=True)
+
+
+def test_headline_full_batch0_and_sampled():
+    w = synthetic.WORKLOADS["headline_f16_1024"]
+    q, k, v = w.inputs()
+    print(f"[fwd] {w.name}", flush=True)
+    o, lse = attention(to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, w.dtype), causal=False, scale=w.scale)
+    o_np, lse_np = to_np(o[:1]), to_np(lse[:1])
+    o_ref, lse_ref = oracle.attention_bits(q[:1], k[:1], v[:1], w.dtype, scale=w.scale)
+    cmp.check_o(o_np, o_ref, w.dtype, "headline b=0 whole")
+    cmp.check_lse(lse_np, lse_ref, "headline b=0 whole")
+    run_sampled(w, 7)
+
+
+LONG = [n for n in synthetic.WORKLOADS if n.startswith("long_")]
+GQA = [n for n in synthetic.WORKLOADS if n.startswith("gqa_")]
+
+
+@pytest.mark.parametrize("name", LONG)
+def test_long_sequence_sampled(name):
+    run_sampled(synthetic.WORKLOADS[name], 11)
+
+
+@pytest.mark.parametrize("name", GQA)
+def test_gqa_head_dim_sweep_sampled(name):
+    run_sampled(synthetic.WORKLOADS[name], 13)
