@@ -102,7 +102,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["fwd", "decode", "all"], default="all")
+    ap.add_argument("--only", choices=["fwd", "headline", "decode", "all"], default="all")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -120,7 +122,14 @@ def main():
 
     # ---- forward, headline workload (the line's value)
     w = synthetic.WORKLOADS["headline_f16_1024"]
-    if args.only in ("fwd", "all"):
+    if args.copy_probe:
+        src = torch.empty(args.copy_probe << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = 2 * src.numel()   # read + write
+        del src, dst
+    if args.only in ("fwd", "headline", "all"):
         q, k, v = upload(w, torch)
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
@@ -143,6 +152,7 @@ def main():
         del q, k, v, o, lse
         torch.cuda.empty_cache()
 
+    if args.only in ("fwd", "all"):
         # forward at N = 4096 (the 50%-of-peak target shape)
         w4 = synthetic.WORKLOADS["long_f16_4096_full"]
         q, k, v = upload(w4, torch)

@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: hipcc emits packed fp32 math on its own otherwise.
-HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+HIPFLAGS = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             f"-I{os.path.join(ROOT, 'include')}"]
 

@@ -91,7 +91,8 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   a.B = B; a.Nq = Nq; a.Nk = Nk; a.Hq = Hq; a.Hkv = Hkv;
   a.group = Hq / Hkv;
   a.n_qtiles = (Nq + fa::kFwdRows - 1) / fa::kFwdRows;
-  a.sl2 = scale * 1.4426950408889634f;
+  a.sl2 = fabsf(scale) * 1.4426950408889634f;
+  a.negate_q = scale < 0.f;
   const int64_t blocks = int64_t(a.n_qtiles) * Hq * B;
   if (blocks > 0x7fffffff) return FA_ERR_SHAPE;
   hipError_t e = fa::launch_fwd(a, d, dtype == FA_BF16, causal != 0, static_cast<hipStream_t>(stream));

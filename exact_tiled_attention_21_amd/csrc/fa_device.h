@@ -126,6 +126,9 @@ __device__ __forceinline__ typename Elem<BF16>::V8 to_v8(const f32x16& x, int ba
   return r;
 }
 
+// Compile-time LDS stage index passed to generic lambdas.
+template <int N> struct Stage { static constexpr int value = N; };
+
 // Workgroup ids are dispatched round-robin over the 8 XCDs; give each XCD a
 // contiguous range of logical ids so the query tiles of one head share that
 // XCD's L2 (and their K/V reads hit it).

@@ -6,10 +6,22 @@
 // loops over all key/value tiles ("flash-attention-v100" README: FlashAttention-2
 // reworked the parallelism and work partitioning). Four waves of 32 rows each;
 // the Q fragment stays in VGPRs for the whole loop; K/V tiles are staged
-// through a double-buffered, XOR-swizzled LDS ring so the loads of tile j+1
-// are in flight while tile j is consumed; the online softmax keeps a running
-// max and sum per row and rescales the O accumulator, so the Nq x Nk scores
-// never leave registers.
+// through a double-buffered, XOR-swizzled LDS ring; the online softmax keeps a
+// running max and sum per row and rescales the O accumulator, so the Nq x Nk
+// scores never leave registers.
+//
+// K/V tiles move from HBM to LDS by DMA (buffer loads that write LDS
+// directly: no staging registers, no LDS store instructions); the swizzle is
+// applied by the choice of global chunk each lane fetches, and rows past the
+// end of the keys read as zero through the buffer bounds check.
+//
+// Per loop step j: issue the DMA of tile j+1 into the stage freed by step
+// j-1; S_j = K_j Q^T on MFMA; softmax; O += V_j P_j on MFMA; wait for this
+// wave's DMA and barrier. Each tile's loads have a whole step to land. The
+// kernel fits in 256 registers so two workgroups share a CU, and the SIMDs
+// interleave one wave's exponentials with the other wave's matrix products. The running max is only moved when a row's max grows by more than
+// 2^kLazy (in log2 units): P then stays below 2^kLazy and the result is
+// unchanged, since O and the row sum share whichever reference max is used.
 #pragma once
 
 #include "fa_device.h"
@@ -27,54 +39,70 @@ template <int D> struct FwdCfg {
   static constexpr int NCB = D / 32;                 // 32-wide d blocks of O^T
   static constexpr int NT = BC / 16;                 // 16-key slices (PV depth)
   static constexpr int TILE_BYTES = BC * D * 2;
-  static constexpr int LDS_BYTES = 2 * 2 * TILE_BYTES;  // 2 stages x (K, V)
-  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  static constexpr int CPT = BC * CPR / THREADS;     // chunks per thread per tensor
+  static constexpr int NDMA = TILE_BYTES / (THREADS * 16);   // 1 KB DMA pieces per wave per tile
   static_assert(BR == kFwdRows, "rows per workgroup");
-  static_assert(BC * CPR % THREADS == 0, "tile must split evenly over threads");
+  static_assert(TILE_BYTES % (THREADS * 16) == 0, "tile must split into whole DMA pieces");
 };
 
-template <int D, bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(256) void fa_fwd_kernel(const FwdArgs a) {
+constexpr float kLazy = 8.0f;   // log2 of the largest unnormalised probability kept
+
+// LDS of one workgroup: two stages each for K and V, as separate objects so the
+// compiler knows a DMA into one stage never feeds a read of the other.
+template <int D> struct FwdLds {
+  static constexpr int TB = FwdCfg<D>::TILE_BYTES;
+  char* k[2];
+  char* v[2];
+};
+
+// Per-wave state and the steps of the tile loop (device code only).
+template <int D, bool BF16, bool CAUSAL> struct FwdWave {
   using C = FwdCfg<D>;
   using E = Elem<BF16>;
   using T = typename E::T;
   using V8 = typename E::V8;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  typedef V8 PF[C::NT];
+  typedef f32x16 SA[C::KB];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int hh = lane >> 5;
-
-  // workgroup -> (query tile, head, batch)
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  int qt = bid % a.n_qtiles;
-  const int hb = bid / a.n_qtiles;
-  const int hq = hb % a.Hq;
-  const int b = hb / a.Hq;
-  if (CAUSAL) qt = a.n_qtiles - 1 - qt;  // longest rows first
-  const int g = hq / a.group;
-
-  const int q0w = qt * C::BR + wave * 32;   // first row of this wave
-  const int qrow = q0w + (lane & 31);       // this lane's query row
-  const int diag = a.Nk - a.Nq;             // query i sees key j iff j <= i + diag
-
-  // Q fragment (B operand): Q[qrow][16s + 8hh .. +7]
+  const FwdArgs& a;
+  int lane, wave, hh, ln32;
+  int qrow, q0w, diag;
+  int ntiles, nt_w, jmask;
+  float sl2;
   V8 qf[C::NS];
-  {
+  f32x16 oacc[C::NCB];
+  float m_run, l_part;
+  // DMA
+  const char* kg;
+  const char* vg;
+  uint32_t rowbytes;
+  int64_t valid;
+  uint32_t goff[C::NDMA];
+  // LDS read offsets
+  uint32_t fk, kro, vxl, vf0, vf1, vb0, vb1;
+
+  __device__ __forceinline__ FwdWave(const FwdArgs& args, int b, int hq, int g, int qt) : a(args) {
+    const int tid = threadIdx.x;
+    lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
+    hh = lane >> 5;
+    ln32 = lane & 31;
+    q0w = qt * C::BR + wave * 32;
+    qrow = q0w + ln32;
+    diag = a.Nk - a.Nq;
+    sl2 = a.sl2;
+
+    // Q fragment (B operand): Q[qrow][16s + 8hh .. +7]; sign-flipped for a negative scale
     const T* qp = reinterpret_cast<const T*>(a.q) +
                   ((static_cast<size_t>(b) * a.Nq + qrow) * a.Hq + hq) * D + 8 * hh;
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) {
       if (qrow < a.Nq) qf[s] = *reinterpret_cast<const V8*>(qp + 16 * s);
       else qf[s] = V8{};
+      if (a.negate_q) qf[s] = -qf[s];
     }
-  }
 
-  // key extents: the workgroup loads tiles up to kend; this wave computes up to wkend
-  int kend = a.Nk, wkend = a.Nk;
-  {
+    // key extents: the workgroup stages tiles up to kend; this wave computes up to wkend
+    int kend = a.Nk, wkend = a.Nk;
     const int last_wg = min(qt * C::BR + C::BR, a.Nq) - 1;
     const int last_w = min(q0w + 32, a.Nq) - 1;
     if (CAUSAL) {
@@ -82,117 +110,158 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(const FwdArgs a) {
       wkend = min(a.Nk, last_w + diag + 1);
     }
     if (q0w >= a.Nq) wkend = 0;
-  }
-  const int ntiles = kend > 0 ? (kend + C::BC - 1) / C::BC : 0;
+    ntiles = kend > 0 ? (kend + C::BC - 1) / C::BC : 0;
+    nt_w = wkend > 0 ? (wkend + C::BC - 1) / C::BC : 0;
+    // first tile that needs an element mask for this wave (key tail or causal diagonal)
+    jmask = (a.Nk % C::BC) ? a.Nk / C::BC : ntiles + 1;
+    if (CAUSAL) jmask = min(jmask, max(0, (q0w + diag + 1) / C::BC));
 
-  // global -> register staging of one K and one V tile
-  const T* kbase = reinterpret_cast<const T*>(a.k) + (static_cast<size_t>(b) * a.Nk * a.Hkv + g) * D;
-  const T* vbase = reinterpret_cast<const T*>(a.v) + (static_cast<size_t>(b) * a.Nk * a.Hkv + g) * D;
-  const size_t rstride = static_cast<size_t>(a.Hkv) * D;
-  u32x4 kst[C::CPT], vst[C::CPT];
-  auto gload = [&](int tile) {
+    // HBM -> LDS by DMA through buffer resources (rows >= Nk read as 0). DMA piece
+    // i of this wave fills LDS bytes [(i * NW + wave) * 1024, +1024): lane l writes
+    // 16 bytes at +16 l, i.e. physical chunk pch of row r, so it fetches logical
+    // chunk pch ^ swz(r) of that row.
+    rowbytes = static_cast<uint32_t>(a.Hkv) * D * 2;
+    const size_t head_off = (static_cast<size_t>(b) * a.Nk * a.Hkv + g) * D * 2;
+    kg = reinterpret_cast<const char*>(a.k) + head_off;
+    vg = reinterpret_cast<const char*>(a.v) + head_off;
+    valid = static_cast<int64_t>(a.Nk - 1) * rowbytes + D * 2;
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int c = tid + i * C::THREADS;
-      const int row = c / C::CPR, x = c % C::CPR;
-      const int key = tile * C::BC + row;
-      if (key < a.Nk) {
-        kst[i] = *reinterpret_cast<const u32x4*>(kbase + key * rstride + 8 * x);
-        vst[i] = *reinterpret_cast<const u32x4*>(vbase + key * rstride + 8 * x);
-      } else {
-        kst[i] = u32x4{0, 0, 0, 0};
-        vst[i] = u32x4{0, 0, 0, 0};
-      }
+    for (int i = 0; i < C::NDMA; ++i) {
+      const uint32_t p = (i * C::NW + wave) * 1024 + lane * 16;
+      const uint32_t r = p / (D * 2), pch = (p % (D * 2)) / 16;
+      goff[i] = r * rowbytes + ((pch ^ Swz<D>::f(r)) << 4);
     }
-  };
-  auto lstore = [&](int stage) {
-    char* kt = smem + stage * 2 * C::TILE_BYTES;
-    char* vt = kt + C::TILE_BYTES;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int c = tid + i * C::THREADS;
-      const uint32_t o = Swz<D>::off(c / C::CPR, c % C::CPR);
-      *reinterpret_cast<u32x4*>(kt + o) = kst[i];
-      *reinterpret_cast<u32x4*>(vt + o) = vst[i];
-    }
-  };
 
-  f32x16 oacc[C::NCB];
-#pragma unroll
-  for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] = f32x16{};
-  float m_run = kNegInf;  // running max of scale*log2(e)*s
-  float l_part = 0.f;     // running sum over this lane's keys
+    // LDS read offsets (the swizzle only sees the low 4 row bits)
+    fk = Swz<D>::f(ln32);
+    kro = ln32 * (D * 2);
+    const uint32_t vj = lane & 15, vcb = (lane >> 4) & 1;
+    const uint32_t vrow0 = 4 * hh + (vj >> 2), vrow1 = vrow0 + 8;
+    vxl = 2 * vcb + ((vj & 3) >> 1);
+    vf0 = Swz<D>::f(vrow0);
+    vf1 = Swz<D>::f(vrow1);
+    vb0 = vrow0 * (D * 2) + 8 * (vj & 1);
+    vb1 = vrow1 * (D * 2) + 8 * (vj & 1);
 
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
+#pragma unroll
+    for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] = f32x16{};
+    m_run = kNegInf;
+    l_part = 0.f;
   }
-  __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int stage = j & 1;
-    if (j + 1 < ntiles) gload(j + 1);
-    const int k0 = j * C::BC;
-    if (k0 < wkend) {
-      const char* kt = smem + stage * 2 * C::TILE_BYTES;
-      const char* vt = kt + C::TILE_BYTES;
-      // S^T = K Q^T
-      f32x16 sacc[C::KB];
+  __device__ __forceinline__ void dma(const char* base, int tile, char* lds) const {
+    const int64_t off = static_cast<int64_t>(tile) * C::BC * rowbytes;
+    const int64_t rem = valid - off;
+    const uint32_t nrec = rem > 0 ? static_cast<uint32_t>(rem > 0x7fffffff ? 0x7fffffff : rem) : 0u;
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(base + (rem > 0 ? off : 0)), 0, nrec, 0x00020000);
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        sacc[kb] = f32x16{};
+    for (int i = 0; i < C::NDMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(lds + (i * C::NW + wave) * 1024), 16, goff[i], 0, 0, 0);
+  }
+
+  __device__ __forceinline__ V8 kfrag(const char* kt, int kb, int s) const {
+    const uint32_t off = kb * 32 * (D * 2) + kro + ((((2u * s) | hh) ^ fk) << 4);
+    return lds_read_v8<V8>(kt, off);
+  }
+  __device__ __forceinline__ V8 vfrag(const char* vt, int cb, int t) const {
+    const uint32_t x = 4u * cb + vxl;
+    const uint32_t lo = t * 16 * (D * 2) + vb0 + ((x ^ vf0) << 4);
+    const uint32_t hi = t * 16 * (D * 2) + vb1 + ((x ^ vf1) << 4);
+    return __builtin_bit_cast(V8, __builtin_shufflevector(lds_read_tr(vt, lo), lds_read_tr(vt, hi),
+                                                          0, 1, 2, 3, 4, 5, 6, 7));
+  }
+
+  // S_j = K_j Q^T
+  __device__ __forceinline__ void qk(const char* kt, SA& sacc) const {
 #pragma unroll
-        for (int s = 0; s < C::NS; ++s) sacc[kb] = E::mfma(k_frag<D, V8>(kt, kb, s, lane), qf[s], sacc[kb]);
-      }
-      // scale, mask, row max
-      const bool need_mask = (k0 + C::BC > a.Nk) || (CAUSAL && k0 + C::BC - 1 > q0w + diag);
-      float mx = kNegInf;
+    for (int kb = 0; kb < C::KB; ++kb) {
+      sacc[kb] = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
+      for (int s = 0; s < C::NS; ++s) sacc[kb] = E::mfma(kfrag(kt, kb, s), qf[s], sacc[kb]);
+    }
+  }
+
+  // mask (if asked), row max of the raw scores, reference update and O rescale,
+  // then the probabilities (as MFMA B operands) and their row sum
+  template <bool MASK>
+  __device__ __forceinline__ void softmax(SA& sacc, PF& pf, int jt) {
+    if (MASK) {
+      const int k0 = jt * C::BC;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = sacc[kb][r] * a.sl2;
-          if (need_mask) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key >= a.Nk || (CAUSAL && key > qrow + diag)) x = kNegInf;
-          }
-          sacc[kb][r] = x;
-          mx = fmaxf(mx, x);
+          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key >= a.Nk || (CAUSAL && key > qrow + diag)) sacc[kb][r] = kNegInf;
         }
-      }
-      mx = halves_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      m_run = m_new;
-      float psum = 0.f;
+    }
+    float mx = kNegInf;
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(sacc[kb][r] - m_use);
-          sacc[kb][r] = p;
-          psum += p;
-        }
-      }
-      l_part = l_part * alpha + psum;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = halves_max(mx);
+    const float mxs = (mx == kNegInf) ? kNegInf : mx * sl2;
+    const bool need = mxs > m_run + kLazy;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+      const float m_new = need ? mxs : m_run;
+      // 1 when this row keeps its reference (also for a row still at -inf), 0 when it had none
+      const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m_run - m_new);
+      l_part *= alpha;
 #pragma unroll
       for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] *= alpha;
-      // O^T += V^T P^T
-#pragma unroll
-      for (int t = 0; t < C::NT; ++t) {
-        const V8 pf = to_v8<BF16>(sacc[t >> 1], 8 * (t & 1));
-#pragma unroll
-        for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] = E::mfma(v_frag<D, V8>(vt, cb, t, lane), pf, oacc[cb]);
-      }
+      m_run = m_new;
     }
-    if (j + 1 < ntiles) lstore(stage ^ 1);
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) {
+      f32x16 tmp;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float sv = sacc[t >> 1][8 * (t & 1) + i];
+        float p = exp2_fast(__builtin_fmaf(sv, sl2, -m_use));
+        if (MASK) p = (sv == kNegInf) ? 0.f : p;
+        psum += p;
+        tmp[i] = p;
+      }
+      pf[t] = to_v8<BF16>(tmp, 0);
+    }
+    l_part += psum;
+  }
+
+  // O += V_j P_j
+  __device__ __forceinline__ void pv(const char* vt, const PF& pf) {
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+      for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] = E::mfma(vfrag(vt, cb, t), pf[t], oacc[cb]);
+  }
+
+  // one step over tile j held in stage ST; tile j+1 is fetched into stage ST^1
+  template <int ST>
+  __device__ __forceinline__ void step(int j, const FwdLds<D>& lds) {
+    if (j + 1 < ntiles) {
+      dma(kg, j + 1, lds.k[ST ^ 1]);
+      dma(vg, j + 1, lds.v[ST ^ 1]);
+    }
+    if (j < nt_w) {
+      SA sacc;
+      PF pf;
+      qk(lds.k[ST], sacc);
+      if (j >= jmask) softmax<true>(sacc, pf, j);
+      else softmax<false>(sacc, pf, j);
+      pv(lds.v[ST], pf);
+    }
     __syncthreads();
   }
 
-  // epilogue: O = O / l, LSE = m + log(l); rows with no visible key give 0 and -inf
-  const float l = halves_sum(l_part);
-  if (qrow < a.Nq) {
+  // O = O / l, LSE = m + log(l); rows with no visible key give 0 and -inf
+  __device__ __forceinline__ void finish(int b, int hq) {
+    const float l = halves_sum(l_part);
+    if (qrow >= a.Nq) return;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     T* op = reinterpret_cast<T*>(a.o) + ((static_cast<size_t>(b) * a.Nq + qrow) * a.Hq + hq) * D;
 #pragma unroll
@@ -210,6 +279,38 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(const FwdArgs a) {
       a.lse[(static_cast<size_t>(b) * a.Hq + hq) * a.Nq + qrow] =
           l > 0.f ? (m_run + __log2f(l)) * kLn2 : kNegInf;
   }
+};
+
+template <int D, bool BF16, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(const FwdArgs a) {
+  using C = FwdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char k_lds0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[C::TILE_BYTES];
+
+  // workgroup -> (query tile, head, batch)
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  int qt = bid % a.n_qtiles;
+  const int hb = bid / a.n_qtiles;
+  const int hq = hb % a.Hq;
+  const int b = hb / a.Hq;
+  if (CAUSAL) qt = a.n_qtiles - 1 - qt;  // longest rows first
+  const int g = hq / a.group;
+
+  FwdWave<D, BF16, CAUSAL> w(a, b, hq, g, qt);
+  const FwdLds<D> lds{{k_lds0, k_lds1}, {v_lds0, v_lds1}};
+  if (w.ntiles > 0) {
+    w.dma(w.kg, 0, lds.k[0]);
+    w.dma(w.vg, 0, lds.v[0]);
+  }
+  __syncthreads();
+  for (int j = 0; j < w.ntiles; j += 2) {
+    w.template step<0>(j, lds);
+    if (j + 1 >= w.ntiles) break;
+    w.template step<1>(j + 1, lds);
+  }
+  w.finish(b, hq);
 }
 
 template <int D>
@@ -217,10 +318,15 @@ hipError_t launch_fwd_d(const FwdArgs& a, bool bf16, bool causal, hipStream_t st
   using C = FwdCfg<D>;
   const dim3 grid(static_cast<unsigned>(a.n_qtiles) * a.Hq * a.B);
   const dim3 block(C::THREADS);
-  const void* fn = bf16 ? (causal ? (const void*)fa_fwd_kernel<D, true, true> : (const void*)fa_fwd_kernel<D, true, false>)
-                        : (causal ? (const void*)fa_fwd_kernel<D, false, true> : (const void*)fa_fwd_kernel<D, false, false>);
-  void* args[] = {const_cast<FwdArgs*>(&a)};
-  return hipLaunchKernel(fn, grid, block, args, C::LDS_BYTES, stream);
+  (void)hipGetLastError();   // start from a clean error state
+  if (bf16) {
+    if (causal) fa_fwd_kernel<D, true, true><<<grid, block, 0, stream>>>(a);
+    else fa_fwd_kernel<D, true, false><<<grid, block, 0, stream>>>(a);
+  } else {
+    if (causal) fa_fwd_kernel<D, false, true><<<grid, block, 0, stream>>>(a);
+    else fa_fwd_kernel<D, false, false><<<grid, block, 0, stream>>>(a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace fa

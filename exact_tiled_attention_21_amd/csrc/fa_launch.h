@@ -15,7 +15,8 @@ struct FwdArgs {
   int B, Nq, Nk, Hq, Hkv;
   int group;       // Hq / Hkv
   int n_qtiles;    // ceil(Nq / rows per workgroup)
-  float sl2;       // scale * log2(e)
+  float sl2;       // |scale| * log2(e)
+  int negate_q;    // scale < 0: the kernel flips the sign of Q instead
 };
 
 struct DecodeArgs {
