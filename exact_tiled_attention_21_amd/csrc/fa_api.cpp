@@ -90,7 +90,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.B = B; a.Nq = Nq; a.Nk = Nk; a.Hq = Hq; a.Hkv = Hkv;
   a.group = Hq / Hkv;
-  a.n_qtiles = (Nq + fa::kFwdRows - 1) / fa::kFwdRows;
+  a.n_qtiles = (Nq + fa::fwd_rows(d) - 1) / fa::fwd_rows(d);
   a.sl2 = fabsf(scale) * 1.4426950408889634f;
   a.negate_q = scale < 0.f;
   const int64_t blocks = int64_t(a.n_qtiles) * Hq * B;

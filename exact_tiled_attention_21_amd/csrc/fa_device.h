@@ -126,6 +126,24 @@ __device__ __forceinline__ typename Elem<BF16>::V8 to_v8(const f32x16& x, int ba
   return r;
 }
 
+// acc + x[2i] + x[2i+1] on the packed pair i of an 8-wide operand (fp32 sum)
+template <bool BF16>
+__device__ __forceinline__ float dot2_ones(typename Elem<BF16>::V8 x, int i, float acc);
+template <>
+__device__ __forceinline__ float dot2_ones<false>(f16x8 x, int i, float acc) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  const h2 v = {x[2 * i], x[2 * i + 1]};
+  return __builtin_amdgcn_fdot2(v, one, acc, false);
+}
+template <>
+__device__ __forceinline__ float dot2_ones<true>(bf16x8 x, int i, float acc) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const b2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  const b2 v = {x[2 * i], x[2 * i + 1]};
+  return __builtin_amdgcn_fdot2_f32_bf16(v, one, acc, false);
+}
+
 // Compile-time LDS stage index passed to generic lambdas.
 template <int N> struct Stage { static constexpr int value = N; };
 

@@ -16,10 +16,10 @@
 // end of the keys read as zero through the buffer bounds check.
 //
 // Per loop step j: issue the DMA of tile j+1 into the stage freed by step
-// j-1; S_j = K_j Q^T on MFMA; softmax; O += V_j P_j on MFMA; wait for this
-// wave's DMA and barrier. Each tile's loads have a whole step to land. The
-// kernel fits in 256 registers so two workgroups share a CU, and the SIMDs
-// interleave one wave's exponentials with the other wave's matrix products. The running max is only moved when a row's max grows by more than
+// j-1; S_j = K_j Q^T on MFMA; softmax; O += V_j P_j on MFMA; barrier. Each
+// tile's loads have a whole step to land. For d <= 128 the kernel fits in 256
+// registers, so two workgroups share a CU and each SIMD can interleave one
+// wave's exponentials with the other wave's matrix products. The running max is only moved when a row's max grows by more than
 // 2^kLazy (in log2 units): P then stays below 2^kLazy and the result is
 // unchanged, since O and the row sum share whichever reference max is used.
 #pragma once
@@ -30,6 +30,9 @@
 namespace fa {
 
 template <int D> struct FwdCfg {
+  // four waves, one per SIMD; for d <= 128 the kernel fits 256 registers so two
+  // workgroups share a CU (two waves per SIMD, each with its own barrier)
+  static constexpr int WPE = (D <= 128) ? 2 : 1;     // waves per SIMD
   static constexpr int NW = 4;                       // waves per workgroup
   static constexpr int THREADS = NW * 64;
   static constexpr int BR = 32 * NW;                 // query rows per workgroup
@@ -39,9 +42,11 @@ template <int D> struct FwdCfg {
   static constexpr int NCB = D / 32;                 // 32-wide d blocks of O^T
   static constexpr int NT = BC / 16;                 // 16-key slices (PV depth)
   static constexpr int TILE_BYTES = BC * D * 2;
-  static constexpr int NDMA = TILE_BYTES / (THREADS * 16);   // 1 KB DMA pieces per wave per tile
-  static_assert(BR == kFwdRows, "rows per workgroup");
-  static_assert(TILE_BYTES % (THREADS * 16) == 0, "tile must split into whole DMA pieces");
+  static constexpr int NPIECE = TILE_BYTES / 1024;           // 1 KB DMA pieces per tile
+  static constexpr int NDMA = (NPIECE + NW - 1) / NW;        // pieces per wave (the last may idle)
+  static constexpr bool EVEN = NPIECE % NW == 0;
+  static_assert(BR == fwd_rows(D), "rows per workgroup");
+  static_assert(TILE_BYTES % 1024 == 0, "tile must split into whole DMA pieces");
 };
 
 constexpr float kLazy = 8.0f;   // log2 of the largest unnormalised probability kept
@@ -78,7 +83,7 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
   int64_t valid;
   uint32_t goff[C::NDMA];
   // LDS read offsets
-  uint32_t fk, kro, vxl, vf0, vf1, vb0, vb1;
+  uint32_t kro, kxo, vb0, vb1, vx0, vx1;
 
   __device__ __forceinline__ FwdWave(const FwdArgs& args, int b, int hq, int g, int qt) : a(args) {
     const int tid = threadIdx.x;
@@ -133,13 +138,15 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
     }
 
     // LDS read offsets (the swizzle only sees the low 4 row bits)
-    fk = Swz<D>::f(ln32);
+    // K: row 32kb + ln32, chunk (2s | hh) ^ swz(ln32) -> byte (kxo ^ 32s) + row offset
     kro = ln32 * (D * 2);
+    kxo = (static_cast<uint32_t>(hh) ^ Swz<D>::f(ln32)) << 4;
+    // V: rows 16t + vrow0 (+8), chunk (4cb + vxl) ^ swz(row) -> byte (vx ^ 64cb) + row offset
     const uint32_t vj = lane & 15, vcb = (lane >> 4) & 1;
     const uint32_t vrow0 = 4 * hh + (vj >> 2), vrow1 = vrow0 + 8;
-    vxl = 2 * vcb + ((vj & 3) >> 1);
-    vf0 = Swz<D>::f(vrow0);
-    vf1 = Swz<D>::f(vrow1);
+    const uint32_t vxl = 2 * vcb + ((vj & 3) >> 1);
+    vx0 = (vxl ^ Swz<D>::f(vrow0)) << 4;
+    vx1 = (vxl ^ Swz<D>::f(vrow1)) << 4;
     vb0 = vrow0 * (D * 2) + 8 * (vj & 1);
     vb1 = vrow1 * (D * 2) + 8 * (vj & 1);
 
@@ -157,36 +164,51 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
         const_cast<char*>(base + (rem > 0 ? off : 0)), 0, nrec, 0x00020000);
 #pragma unroll
     for (int i = 0; i < C::NDMA; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(lds + (i * C::NW + wave) * 1024), 16, goff[i], 0, 0, 0);
+      if (C::EVEN || i * C::NW + wave < C::NPIECE)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(lds + (i * C::NW + wave) * 1024), 16, goff[i], 0, 0, 0);
   }
 
+  // LDS fragment addresses: the XOR depends on the lane and the d slice, so
+  // each one costs one ALU op; keeping them all live would cost 16 registers.
   __device__ __forceinline__ V8 kfrag(const char* kt, int kb, int s) const {
-    const uint32_t off = kb * 32 * (D * 2) + kro + ((((2u * s) | hh) ^ fk) << 4);
+    const uint32_t off = kb * 32 * (D * 2) + ((kxo ^ (32u * s)) + kro);
     return lds_read_v8<V8>(kt, off);
   }
   __device__ __forceinline__ V8 vfrag(const char* vt, int cb, int t) const {
-    const uint32_t x = 4u * cb + vxl;
-    const uint32_t lo = t * 16 * (D * 2) + vb0 + ((x ^ vf0) << 4);
-    const uint32_t hi = t * 16 * (D * 2) + vb1 + ((x ^ vf1) << 4);
+    const uint32_t lo = t * 16 * (D * 2) + ((vx0 ^ (64u * cb)) + vb0);
+    const uint32_t hi = t * 16 * (D * 2) + ((vx1 ^ (64u * cb)) + vb1);
     return __builtin_bit_cast(V8, __builtin_shufflevector(lds_read_tr(vt, lo), lds_read_tr(vt, hi),
                                                           0, 1, 2, 3, 4, 5, 6, 7));
   }
 
-  // S_j = K_j Q^T
+  // S_j = K_j Q^T (K fragments from LDS, Q from registers). K fragments are read
+  // kPre MFMAs ahead through a small rolling buffer; the order is pinned for the
+  // scheduler, which would otherwise issue each read right before its MFMA.
+  static constexpr int kQkMf = C::KB * C::NS;            // MFMAs in S_j
+  static constexpr int kPre = kQkMf < 4 ? kQkMf : 4;     // K fragments in flight
   __device__ __forceinline__ void qk(const char* kt, SA& sacc) const {
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-      sacc[kb] = f32x16{};
+    for (int kb = 0; kb < C::KB; ++kb) sacc[kb] = f32x16{};
+    V8 kf[kPre];
 #pragma unroll
-      for (int s = 0; s < C::NS; ++s) sacc[kb] = E::mfma(kfrag(kt, kb, s), qf[s], sacc[kb]);
+    for (int i = 0; i < kPre; ++i) kf[i] = kfrag(kt, i % C::KB, i / C::KB);
+#pragma unroll
+    for (int i = 0; i < kQkMf; ++i) {
+      sacc[i % C::KB] = E::mfma(kf[i % kPre], qf[i / C::KB], sacc[i % C::KB]);
+      if (i + kPre < kQkMf) kf[i % kPre] = kfrag(kt, (i + kPre) % C::KB, (i + kPre) / C::KB);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+#pragma unroll
+    for (int i = 0; i < kQkMf; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + kPre < kQkMf) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   }
 
-  // mask (if asked), row max of the raw scores, reference update and O rescale,
-  // then the probabilities (as MFMA B operands) and their row sum
+  // mask (if asked) and row max of the raw scores of tile jt
   template <bool MASK>
-  __device__ __forceinline__ void softmax(SA& sacc, PF& pf, int jt) {
+  __device__ __forceinline__ float rowmax(SA& sacc, int jt) const {
     if (MASK) {
       const int k0 = jt * C::BC;
 #pragma unroll
@@ -202,7 +224,11 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = halves_max(mx);
+    return halves_max(mx);
+  }
+  // move the reference max if the tile's max exceeds it by more than 2^kLazy
+  // (rare after the first tiles), rescaling O and the row sum
+  __device__ __forceinline__ void rebase(float mx) {
     const float mxs = (mx == kNegInf) ? kNegInf : mx * sl2;
     const bool need = mxs > m_run + kLazy;
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
@@ -214,8 +240,14 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
       for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] *= alpha;
       m_run = m_new;
     }
+  }
+  // probabilities of a tile (as MFMA B operands, rounded to the element type) and
+  // their row sum, accumulated in fp32 from the unrounded values: summing the
+  // rounded bf16 values would put up to 2^-9 relative error into the LSE
+  template <bool MASK>
+  __device__ __forceinline__ void probs(const SA& sacc, PF& pf) {
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-    float psum = 0.f;
+    float psum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
       f32x16 tmp;
@@ -224,25 +256,48 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
         const float sv = sacc[t >> 1][8 * (t & 1) + i];
         float p = exp2_fast(__builtin_fmaf(sv, sl2, -m_use));
         if (MASK) p = (sv == kNegInf) ? 0.f : p;
-        psum += p;
+        psum[i & 3] += p;
         tmp[i] = p;
       }
       pf[t] = to_v8<BF16>(tmp, 0);
     }
-    l_part += psum;
+    l_part += (psum[0] + psum[1]) + (psum[2] + psum[3]);
   }
 
-  // O += V_j P_j
+  // O += V_j P_j, with the transposing reads of V one MFMA ahead
+  static constexpr int kPvMf = C::NT * C::NCB;
   __device__ __forceinline__ void pv(const char* vt, const PF& pf) {
+    V8 vf[2];
+    vf[0] = vfrag(vt, 0, 0);
 #pragma unroll
-    for (int t = 0; t < C::NT; ++t)
+    for (int i = 0; i < kPvMf; ++i) {
+      if (i + 1 < kPvMf) vf[(i + 1) & 1] = vfrag(vt, (i + 1) % C::NCB, (i + 1) / C::NCB);
+      oacc[i % C::NCB] = E::mfma(vf[i & 1], pf[i / C::NCB], oacc[i % C::NCB]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] = E::mfma(vfrag(vt, cb, t), pf[t], oacc[cb]);
+    for (int i = 0; i < kPvMf; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + 2 < kPvMf) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
   }
 
-  // one step over tile j held in stage ST; tile j+1 is fetched into stage ST^1
+  // Finish tile jt: mask, max, reference update, probabilities.
+  __device__ __forceinline__ void softmax(SA& sacc, PF& pf, int jt) {
+    if (jt >= jmask) {
+      rebase(rowmax<true>(sacc, jt));
+      probs<true>(sacc, pf);
+    } else {
+      rebase(rowmax<false>(sacc, jt));
+      probs<false>(sacc, pf);
+    }
+  }
+
+  // One step over tile j (stage ST); the DMA started here fills tile j+1 into
+  // stage ST^1, which was last read in step j-1.
   template <int ST>
   __device__ __forceinline__ void step(int j, const FwdLds<D>& lds) {
+    asm volatile("" : "+v"(kxo), "+v"(vx0), "+v"(vx1));
     if (j + 1 < ntiles) {
       dma(kg, j + 1, lds.k[ST ^ 1]);
       dma(vg, j + 1, lds.v[ST ^ 1]);
@@ -251,8 +306,7 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
       SA sacc;
       PF pf;
       qk(lds.k[ST], sacc);
-      if (j >= jmask) softmax<true>(sacc, pf, j);
-      else softmax<false>(sacc, pf, j);
+      softmax(sacc, pf, j);
       pv(lds.v[ST], pf);
     }
     __syncthreads();
@@ -282,7 +336,8 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
 };
 
 template <int D, bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(FwdCfg<D>::THREADS)
+__attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fa_fwd_kernel(const FwdArgs a) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) char k_lds0[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char k_lds1[C::TILE_BYTES];

@@ -35,8 +35,8 @@ struct DecodeArgs {
   float sl2;       // scale * log2(e)
 };
 
-// Rows of queries one forward workgroup covers.
-constexpr int kFwdRows = 128;
+// Rows of queries one forward workgroup covers (32 per wave).
+constexpr int fwd_rows(int) { return 128; }
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
