@@ -72,6 +72,12 @@ fa_status check_common(const void* q, const void* k, const void* v, void* o, con
 
 size_t pad256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// each requested chunk is processed as up to this many sub-chunks, each with its
+// own partial (the workspace is sized for the maximum)
+constexpr int kSubPerChunk = 4;
+// single-wave workgroups that give the chip about one round (256 CUs x 4 SIMDs)
+constexpr int64_t kDecodeWaves = 1024;
+
 int decode_chunk(int Nk, int splits) {
   const int per = (Nk + splits - 1) / splits;
   return (per + 31) / 32 * 32;
@@ -102,7 +108,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 size_t fa_decode_workspace_bytes(int B, int Nq, int Hq, int d, int num_splits) {
   if (B < 1 || Nq < 1 || Hq < 1 || !head_dim_ok(d) || num_splits < 1 || num_splits > FA_MAX_SPLITS)
     return 0;
-  const size_t rows = size_t(num_splits) * B * Hq * Nq;
+  const size_t rows = size_t(kSubPerChunk) * num_splits * B * Hq * Nq;
   return pad256(rows * d * sizeof(float)) + pad256(rows * sizeof(float));
 }
 
@@ -119,16 +125,21 @@ fa_status fa_decode_splitkv(const void* q, const void* k_cache, const void* v_ca
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
   const int group = Hq / Hkv;
   const int64_t row_blocks = (int64_t(group) * Nq + 31) / 32;
-  if (row_blocks * Hkv > 65535 || B > 65535) return FA_ERR_SHAPE;  // grid y / z limits
+  if (int64_t(kSubPerChunk) * num_splits > 65535 || B > 65535) return FA_ERR_SHAPE;  // grid y / z limits
+  if (row_blocks * Hkv > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (int64_t(Nk) * Hkv * d * 2 > 0x7fffffffLL) return FA_ERR_SHAPE;   // 32-bit buffer offsets
   fa::DecodeArgs a;
   a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse;
-  const size_t rows = size_t(num_splits) * B * Hq * Nq;
+  const size_t rows = size_t(kSubPerChunk) * num_splits * B * Hq * Nq;
   a.part_o = static_cast<float*>(workspace);
   a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pad256(rows * d * sizeof(float)));
   a.B = B; a.Nq = Nq; a.Nk = Nk; a.Hq = Hq; a.Hkv = Hkv;
   a.group = group;
-  a.splits = num_splits;
+  const int64_t units = int64_t(num_splits) * Hkv * row_blocks * B;
+  a.sub_per = units >= kDecodeWaves ? 1 : (2 * units >= kDecodeWaves ? 2 : kSubPerChunk);
+  a.splits = a.sub_per * num_splits;
   a.chunk = decode_chunk(Nk, num_splits);
+  a.sub = (((a.chunk + a.sub_per - 1) / a.sub_per) + 31) / 32 * 32;
   a.row_blocks = static_cast<int>(row_blocks);
   a.sl2 = scale * 1.4426950408889634f;
   hipError_t e = fa::launch_decode(a, d, dtype == FA_BF16, causal != 0, static_cast<hipStream_t>(stream));

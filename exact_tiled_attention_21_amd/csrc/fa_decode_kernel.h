@@ -7,16 +7,17 @@
 // every chunk in parallel while writing one extra scalar per row and chunk
 // (the log-sum-exp), then combine.
 //
-// Split kernel: one workgroup per (chunk, KV head, batch[, row block]). The
-// query rows of the whole GQA group (Hq/Hkv heads x Nq positions, at most 32
-// per row block) share the chunk's K/V, which is therefore read from HBM once.
-// The four waves take interleaved 32-key tiles of the chunk. K fragments are
-// loaded straight from global memory into MFMA A-operand registers (no LDS);
-// V tiles go through a small wave-private, swizzled LDS tile so the
-// transposing read can build the V^T operand. Loads of a wave's next tile are
-// issued before the current one is consumed. The four waves' (max, sum, O)
-// states are merged through LDS and written as one normalised fp32 partial and
-// its log-sum-exp per row.
+// Split kernel: each chunk is processed as 1, 2 or 4 sub-chunks (enough to give
+// the chip about one round of waves), one single-wave workgroup per (sub-chunk,
+// KV head, batch[, row block]). The query rows of the
+// whole GQA group (Hq/Hkv heads x Nq positions, at most 32 per row block) share
+// the sub-chunk's K/V, which is therefore read from HBM once. The wave streams
+// its 32-key tiles with fully coalesced 16-byte loads into a ring of two tiles
+// in registers, stages each tile through its own swizzled LDS tiles (K for the
+// A operand, V for the transposing read), and writes one normalised fp32
+// partial and its log-sum-exp per row; the combine kernel merges the
+// sub-chunk partials of every chunk with the other chunks'. No barriers: up to
+// four such waves share a CU, one per SIMD.
 //
 // Combine kernel: per output row, LSE = log sum_s exp(LSE_s) and
 // O = sum_s exp(LSE_s - LSE) O_s; chunks with LSE_s = -inf weigh nothing.
@@ -28,215 +29,292 @@
 namespace fa {
 
 template <int D> struct DecCfg {
-  static constexpr int NW = 4;
-  static constexpr int THREADS = NW * 64;
-  static constexpr int BC = 32;                 // keys per wave tile
-  static constexpr int NS = D / 16;
-  static constexpr int NCB = D / 32;
-  static constexpr int CPR = D / 8;             // 16-byte chunks per row
-  static constexpr int VCPL = BC * CPR / 64;    // V chunks per lane per tile
-  static constexpr int VTILE = BC * D * 2;      // bytes of one wave's V tile
-  static constexpr int MERGE = (NW - 1) * (NCB * 16 + 2) * 64 * 4;  // published wave states
-  static constexpr int LDS_BYTES = (NW * VTILE > MERGE) ? NW * VTILE : MERGE;
+  static constexpr int BC = 32;                   // keys per tile
+  static constexpr int NS = D / 16;               // 16-wide d slices (QK^T depth)
+  static constexpr int NCB = D / 32;              // 32-wide d blocks of O^T
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  static constexpr int NCH = BC * CPR / 64;       // 16-byte chunks per lane per tensor per tile
+  static constexpr int TILE = BC * D * 2;         // bytes of one K or V tile
+  static constexpr int NSLOT = (D <= 128) ? 2 : 1;  // tiles in flight in registers
 };
 
-template <int D, bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(256) void fa_decode_split_kernel(const DecodeArgs a) {
+// One wave per workgroup: it streams the keys of one sub-chunk.
+template <int D, bool BF16, bool CAUSAL> struct DecWave {
   using C = DecCfg<D>;
   using E = Elem<BF16>;
   using T = typename E::T;
   using V8 = typename E::V8;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  typedef u32x4 Stage[C::NCH];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
-  const int split = blockIdx.x;
-  const int g = blockIdx.y % a.Hkv;
-  const int rb = blockIdx.y / a.Hkv;
-  const int b = blockIdx.z;
-  const int R = a.group * a.Nq;             // rows of this KV head group
-  const int diag = a.Nk - a.Nq;
-
-  // row r = i * group + (hq - g * group): consecutive rows are adjacent heads
-  const int r = rb * 32 + (lane & 31);
-  const bool rvalid = r < R;
-  const int ri = rvalid ? r / a.group : 0;
-  const int rhq = g * a.group + (rvalid ? r % a.group : 0);
-
+  const DecodeArgs& a;
+  int lane, hh;
+  bool rvalid;
+  int ri, rhq, diag, i_first, k_lo, k_hi, ntile;
+  float sl2;
   V8 qf[C::NS];
-  {
+  f32x16 oacc[C::NCB];
+  float m_run, l_part;
+  const char* kg;
+  const char* vg;
+  uint32_t rowbytes;
+  int64_t valid;
+  uint32_t goff;                // this lane's first 16-byte piece of a tile (coalesced rows)
+  uint32_t kro, kxo, vb0, vb1, vx0, vx1;   // LDS fragment read offsets
+
+  __device__ __forceinline__ DecWave(const DecodeArgs& args, int part, int g, int rb, int b) : a(args) {
+    lane = threadIdx.x & 63;
+    hh = lane >> 5;
+    const int R = a.group * a.Nq;               // rows of this KV head group
+    diag = a.Nk - a.Nq;
+    // row r = i * group + (hq - g * group): consecutive rows are adjacent heads
+    const int r = rb * 32 + (lane & 31);
+    rvalid = r < R;
+    ri = rvalid ? r / a.group : 0;
+    rhq = g * a.group + (rvalid ? r % a.group : 0);
+    sl2 = a.sl2;
     const T* qp = reinterpret_cast<const T*>(a.q) +
                   ((static_cast<size_t>(b) * a.Nq + ri) * a.Hq + rhq) * D + 8 * hh;
 #pragma unroll
-    for (int s = 0; s < C::NS; ++s) {
-      if (rvalid) qf[s] = *reinterpret_cast<const V8*>(qp + 16 * s);
-      else qf[s] = V8{};
+    for (int s = 0; s < C::NS; ++s) qf[s] = rvalid ? *reinterpret_cast<const V8*>(qp + 16 * s) : V8{};
+
+    // keys of this sub-chunk: chunk part / sub_per, piece part % sub_per; clipped
+    // by the chunk, the cache length and (causal) the last row
+    const int c_lo = (part / a.sub_per) * a.chunk;
+    const int c_hi = min(a.Nk, c_lo + a.chunk);
+    k_lo = c_lo + (part % a.sub_per) * a.sub;
+    k_hi = min(c_hi, k_lo + a.sub);
+    i_first = (rb * 32) / a.group;
+    if (CAUSAL) {
+      const int i_last = (min(R, rb * 32 + 32) - 1) / a.group;
+      k_hi = min(k_hi, i_last + diag + 1);
     }
+    ntile = k_hi > k_lo ? (k_hi - k_lo + C::BC - 1) / C::BC : 0;
+
+    rowbytes = static_cast<uint32_t>(a.Hkv) * D * 2;
+    const size_t head_off = (static_cast<size_t>(b) * a.Nk * a.Hkv + g) * D * 2;
+    kg = reinterpret_cast<const char*>(a.k) + head_off;
+    vg = reinterpret_cast<const char*>(a.v) + head_off;
+    valid = static_cast<int64_t>(a.Nk - 1) * rowbytes + D * 2;
+    // offset of this lane's first piece of a tile (see goff_of)
+    goff = static_cast<uint32_t>(lane / C::CPR) * rowbytes + static_cast<uint32_t>(lane % C::CPR) * 16;
+
+    kro = static_cast<uint32_t>(lane & 31) * (D * 2);
+    kxo = (static_cast<uint32_t>(hh) ^ Swz<D>::f(lane & 31)) << 4;
+    const uint32_t vj = lane & 15, vcb = (lane >> 4) & 1;
+    const uint32_t vrow0 = 4 * hh + (vj >> 2), vrow1 = vrow0 + 8;
+    const uint32_t vxl = 2 * vcb + ((vj & 3) >> 1);
+    vx0 = (vxl ^ Swz<D>::f(vrow0)) << 4;
+    vx1 = (vxl ^ Swz<D>::f(vrow1)) << 4;
+    vb0 = vrow0 * (D * 2) + 8 * (vj & 1);
+    vb1 = vrow1 * (D * 2) + 8 * (vj & 1);
+#pragma unroll
+    for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] = f32x16{};
+    m_run = kNegInf;
+    l_part = 0.f;
   }
 
-  // keys of this chunk, clipped by the cache length and (causal) the last row
-  const int k_lo = split * a.chunk;
-  int k_hi = min(a.Nk, k_lo + a.chunk);
-  int i_first = (rb * 32) / a.group;                    // smallest query position
-  if (CAUSAL) {
-    const int i_last = (min(R, rb * 32 + 32) - 1) / a.group;
-    k_hi = min(k_hi, i_last + diag + 1);
+  // K and V rows of tile t into registers, 16 lanes per 256-byte row (coalesced);
+  // rows past the cache read as zero through the buffer bounds check
+  __device__ __forceinline__ void load(int t, Stage& ks, Stage& vs) const {
+    const int64_t off = static_cast<int64_t>(k_lo + t * C::BC) * rowbytes;
+    const int64_t rem = valid - off;
+    const uint32_t nrec = rem > 0 ? static_cast<uint32_t>(rem > 0x7fffffff ? 0x7fffffff : rem) : 0u;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(kg + (rem > 0 ? off : 0)), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(vg + (rem > 0 ? off : 0)), 0, nrec, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < C::NCH; ++i) {
+      const uint32_t o = goff_of(i);
+      ks[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
+      vs[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+    }
   }
-  const int ntile = k_hi > k_lo ? (k_hi - k_lo + C::BC - 1) / C::BC : 0;
-
-  const size_t rstride = static_cast<size_t>(a.Hkv) * D;
-  const T* kbase = reinterpret_cast<const T*>(a.k) + (static_cast<size_t>(b) * a.Nk * a.Hkv + g) * D;
-  const T* vbase = reinterpret_cast<const T*>(a.v) + (static_cast<size_t>(b) * a.Nk * a.Hkv + g) * D;
-  char* vt = smem + wave * C::VTILE;
-
-  V8 kf[C::NS];
-  u32x4 vst[C::VCPL];
-  auto gload = [&](int tile) {
-    const int key = k_lo + tile * C::BC + (lane & 31);
-    const bool ok = key < k_hi;
-    const T* kp = kbase + static_cast<size_t>(ok ? key : 0) * rstride + 8 * hh;
+  // piece i of a tile is 16-byte chunk c = lane + 64 i of the tile: row c / CPR, chunk c % CPR
+  static constexpr bool kEvenRows = (64 % C::CPR) == 0;   // d = 32, 64, 128, 256
+  __device__ __forceinline__ uint32_t goff_of(int i) const {
+    if (kEvenRows) return goff + static_cast<uint32_t>((64 * i) / C::CPR) * rowbytes;
+    const uint32_t c = lane + 64 * i;
+    return (c / C::CPR) * rowbytes + (c % C::CPR) * 16;
+  }
+  // registers -> the wave's swizzled LDS tiles
+  __device__ __forceinline__ void stage(const Stage& ks, const Stage& vs, char* kt, char* vt) const {
 #pragma unroll
-    for (int s = 0; s < C::NS; ++s) kf[s] = ok ? *reinterpret_cast<const V8*>(kp + 16 * s) : V8{};
-#pragma unroll
-    for (int i = 0; i < C::VCPL; ++i) {
-      const int c = lane + 64 * i;
-      const int vkey = k_lo + tile * C::BC + c / C::CPR;
-      vst[i] = vkey < k_hi ? *reinterpret_cast<const u32x4*>(vbase + static_cast<size_t>(vkey) * rstride + 8 * (c % C::CPR))
-                           : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < C::NCH; ++i) {
+      const uint32_t c = lane + 64 * i;
+      const uint32_t o = Swz<D>::off(c / C::CPR, c % C::CPR);
+      *reinterpret_cast<u32x4*>(kt + o) = ks[i];
+      *reinterpret_cast<u32x4*>(vt + o) = vs[i];
     }
-  };
+  }
+  __device__ __forceinline__ V8 kfrag(const char* kt, int s) const {
+    return lds_read_v8<V8>(kt, (kxo ^ (32u * s)) + kro);
+  }
+  __device__ __forceinline__ V8 vfrag(const char* vt, int cb, int t) const {
+    const uint32_t lo = t * 16 * (D * 2) + ((vx0 ^ (64u * cb)) + vb0);
+    const uint32_t hi = t * 16 * (D * 2) + ((vx1 ^ (64u * cb)) + vb1);
+    return __builtin_bit_cast(V8, __builtin_shufflevector(lds_read_tr(vt, lo), lds_read_tr(vt, hi),
+                                                          0, 1, 2, 3, 4, 5, 6, 7));
+  }
 
-  f32x16 oacc[C::NCB];
-#pragma unroll
-  for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] = f32x16{};
-  float m_run = kNegInf, l_part = 0.f;
-
-  int tile = wave;
-  if (tile < ntile) gload(tile);
-  for (; tile < ntile; tile += C::NW) {
-    // stage V of this tile; the current K fragment moves out of the prefetch registers
-    V8 kc[C::NS];
-#pragma unroll
-    for (int s = 0; s < C::NS; ++s) kc[s] = kf[s];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int i = 0; i < C::VCPL; ++i) {
-      const int c = lane + 64 * i;
-      *reinterpret_cast<u32x4*>(vt + Swz<D>::off(c / C::CPR, c % C::CPR)) = vst[i];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (tile + C::NW < ntile) gload(tile + C::NW);
-
-    const int k0 = k_lo + tile * C::BC;
+  // one 32-key tile from the LDS tiles: scores, online softmax, O += V P
+  template <bool MASK>
+  __device__ __forceinline__ void tile(int t, const char* kt, const char* vt) {
+    const int k0 = k_lo + t * C::BC;
     f32x16 sacc = f32x16{};
 #pragma unroll
-    for (int s = 0; s < C::NS; ++s) sacc = E::mfma(kc[s], qf[s], sacc);
-    const bool need_mask = (k0 + C::BC > k_hi) || (CAUSAL && k0 + C::BC - 1 > i_first + diag);
+    for (int s = 0; s < C::NS; ++s) sacc = E::mfma(kfrag(kt, s), qf[s], sacc);
+    if (MASK) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int key = k0 + 8 * (q >> 2) + 4 * hh + (q & 3);
+        if (key >= k_hi || (CAUSAL && key > ri + diag)) sacc[q] = kNegInf;
+      }
+    }
     float mx = kNegInf;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      float x = sacc[q] * a.sl2;
-      if (need_mask) {
-        const int key = k0 + 8 * (q >> 2) + 4 * hh + (q & 3);
-        if (key >= k_hi || (CAUSAL && key > ri + diag)) x = kNegInf;
-      }
-      sacc[q] = x;
-      mx = fmaxf(mx, x);
-    }
+    for (int q = 0; q < 16; ++q) mx = fmaxf(mx, sacc[q]);
     mx = halves_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = exp2_fast(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.f;
+    const float mxs = (mx == kNegInf) ? kNegInf : mx * sl2;
+    const bool need = mxs > m_run + 8.0f;   // reference max moves by more than 2^8 (or is set)
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+      const float m_new = need ? mxs : m_run;
+      const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m_run - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    float psum[2] = {0.f, 0.f};
+    f32x16 p;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const float p = exp2_fast(sacc[q] - m_use);
-      sacc[q] = p;
-      psum += p;
+      float e = exp2_fast(__builtin_fmaf(sacc[q], sl2, -m_use));
+      if (MASK) e = (sacc[q] == kNegInf) ? 0.f : e;
+      p[q] = e;
+      psum[q & 1] += e;
     }
-    l_part = l_part * alpha + psum;
+    l_part += psum[0] + psum[1];
 #pragma unroll
-    for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] *= alpha;
+    for (int tt = 0; tt < 2; ++tt) {
+      const V8 pf = to_v8<BF16>(p, 8 * tt);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const V8 pf = to_v8<BF16>(sacc, 8 * t);
-#pragma unroll
-      for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] = E::mfma(v_frag<D, V8>(vt, cb, t, lane), pf, oacc[cb]);
+      for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] = E::mfma(vfrag(vt, cb, tt), pf, oacc[cb]);
+    }
+  }
+  __device__ __forceinline__ void tile_any(int t, const char* kt, const char* vt) {
+    const int k0 = k_lo + t * C::BC;
+    if ((k0 + C::BC > k_hi) || (CAUSAL && k0 + C::BC - 1 > i_first + diag)) tile<true>(t, kt, vt);
+    else tile<false>(t, kt, vt);
+  }
+};
+
+// LDS writes of this wave must land before its reads, and its reads before the
+// next writes: LDS executes one wave's operations in order, so only the
+// compiler must be kept from moving them across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D, bool BF16, bool CAUSAL>
+__global__ __launch_bounds__(64) void fa_decode_split_kernel(const DecodeArgs a) {
+  using C = DecCfg<D>;
+  using W = DecWave<D, BF16, CAUSAL>;
+  __shared__ __attribute__((aligned(1024))) char kt[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char vt[C::TILE];
+
+  // the KV heads of one key range are consecutive in dispatch order: their rows
+  // interleave in memory, so reading them together keeps DRAM pages open
+  const int part = blockIdx.y;            // chunk * sub_per + piece
+  const int g = blockIdx.x % a.Hkv;
+  const int rb = blockIdx.x / a.Hkv;
+  const int b = blockIdx.z;
+  W w(a, part, g, rb, b);
+
+  // tiles t of the sub-chunk; the loads run NSLOT tiles ahead in registers and
+  // are issued for every tile slot (past the end they read zeros), so each
+  // tile's wait covers exactly its own loads
+  typename W::Stage ks0, vs0, ks1, vs1;
+  w.load(0, ks0, vs0);
+  if (C::NSLOT == 2) w.load(1, ks1, vs1);
+  for (int t = 0; t < w.ntile; t += C::NSLOT) {
+    w.stage(ks0, vs0, kt, vt);
+    wave_lds_sync();
+    w.load(t + C::NSLOT, ks0, vs0);
+    w.tile_any(t, kt, vt);
+    wave_lds_sync();
+    if (C::NSLOT == 2) {
+      if (t + 1 >= w.ntile) break;
+      w.stage(ks1, vs1, kt, vt);
+      wave_lds_sync();
+      w.load(t + 3, ks1, vs1);
+      w.tile_any(t + 1, kt, vt);
+      wave_lds_sync();
     }
   }
 
-  // merge the waves: all of them hold (row, column) at the same lane and
-  // register, so waves 1..3 publish their raw state lane-major and wave 0
-  // folds it into its own registers
-  __syncthreads();  // every wave is done with its V tile
-  constexpr int NV = C::NCB * 16;                          // O values per lane
-  float* pub = reinterpret_cast<float*>(smem);             // [NW-1][NV+2][64]
-  if (wave > 0) {
-    float* mine = pub + (wave - 1) * (NV + 2) * 64 + lane;
-#pragma unroll
-    for (int cb = 0; cb < C::NCB; ++cb)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) mine[(cb * 16 + q) * 64] = oacc[cb][q];
-    mine[NV * 64] = m_run;
-    mine[(NV + 1) * 64] = l_part;
-  }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int w = 1; w < C::NW; ++w) {
-    const float* other = pub + (w - 1) * (NV + 2) * 64 + lane;
-    const float m_o = other[NV * 64];
-    const float m_new = fmaxf(m_run, m_o);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float a0 = exp2_fast(m_run - m_use), a1 = exp2_fast(m_o - m_use);
-    l_part = l_part * a0 + other[(NV + 1) * 64] * a1;
-#pragma unroll
-    for (int cb = 0; cb < C::NCB; ++cb)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) oacc[cb][q] = oacc[cb][q] * a0 + other[(cb * 16 + q) * 64] * a1;
-    m_run = m_new;
-  }
-  const float l = halves_sum(l_part);
-  if (!rvalid) return;
+  // normalised partial and its log2-sum-exp; a sub-chunk with no visible key
+  // writes O = 0, LSE = -inf
+  const float l = halves_sum(w.l_part);
+  if (!w.rvalid) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  const size_t prow = ((static_cast<size_t>(split) * a.B + b) * a.Hq + rhq) * a.Nq + ri;
+  const size_t prow = ((static_cast<size_t>(part) * a.B + b) * a.Hq + w.rhq) * a.Nq + w.ri;
   float* po = a.part_o + prow * D;
 #pragma unroll
   for (int cb = 0; cb < C::NCB; ++cb)
 #pragma unroll
     for (int gr = 0; gr < 4; ++gr) {
-      f32x4 w;
+      f32x4 o4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = oacc[cb][4 * gr + e] * inv;
-      *reinterpret_cast<f32x4*>(po + 32 * cb + 8 * gr + 4 * hh) = w;
+      for (int e = 0; e < 4; ++e) o4[e] = w.oacc[cb][4 * gr + e] * inv;
+      *reinterpret_cast<f32x4*>(po + 32 * cb + 8 * gr + 4 * w.hh) = o4;
     }
-  if (hh == 0) a.part_lse[prow] = l > 0.f ? m_run + __log2f(l) : kNegInf;
+  if (w.hh == 0) a.part_lse[prow] = l > 0.f ? w.m_run + __log2f(l) : kNegInf;
 }
 
 // One row of the output per D/4 threads: O = sum_s w_s O_s with
 // w_s = exp(LSE_s - LSE), LSE = log sum_s exp(LSE_s) (log2 domain inside).
+// Splits are taken 16 at a time with every load of a batch issued at once.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void fa_decode_combine_kernel(const DecodeArgs a) {
   using T = typename Elem<BF16>::T;
   constexpr int TPR = D / 4;
   constexpr int RPB = 256 / TPR;
+  constexpr int SB = 16;
   const int rows = a.B * a.Hq * a.Nq;
   const int row = blockIdx.x * RPB + threadIdx.x / TPR;
   if (row >= rows) return;
   const int c4 = (threadIdx.x % TPR) * 4;
   const size_t stride = static_cast<size_t>(rows);   // elements between splits
   float mx = kNegInf;
-  for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.part_lse[s * stride + row]);
+  for (int s0 = 0; s0 < a.splits; s0 += SB) {
+    float l[SB];
+#pragma unroll
+    for (int i = 0; i < SB; ++i) l[i] = (s0 + i < a.splits) ? a.part_lse[(s0 + i) * stride + row] : kNegInf;
+#pragma unroll
+    for (int i = 0; i < SB; ++i) mx = fmaxf(mx, l[i]);
+  }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float tot = 0.f;
   if (mx != kNegInf) {
-    for (int s = 0; s < a.splits; ++s) {
-      const float w = exp2_fast(a.part_lse[s * stride + row] - mx);
-      tot += w;
-      acc += w * *reinterpret_cast<const f32x4*>(a.part_o + (s * stride + row) * D + c4);
+    for (int s0 = 0; s0 < a.splits; s0 += SB) {
+      float l[SB];
+      f32x4 o[SB];
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const bool ok = s0 + i < a.splits;
+        l[i] = ok ? a.part_lse[(s0 + i) * stride + row] : kNegInf;
+        o[i] = ok ? *reinterpret_cast<const f32x4*>(a.part_o + ((s0 + i) * stride + row) * D + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const float wgt = exp2_fast(l[i] - mx);   // 0 for an empty chunk (-inf)
+        tot += wgt;
+        acc += wgt * o[i];
+      }
     }
     acc *= 1.f / tot;
   }
@@ -255,24 +333,23 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(const DecodeArgs
 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, bool bf16, bool causal, hipStream_t stream) {
-  using C = DecCfg<D>;
-  const dim3 grid1(a.splits, a.Hkv * a.row_blocks, a.B);
-  const void* f1 = bf16 ? (causal ? (const void*)fa_decode_split_kernel<D, true, true>
-                                  : (const void*)fa_decode_split_kernel<D, true, false>)
-                        : (causal ? (const void*)fa_decode_split_kernel<D, false, true>
-                                  : (const void*)fa_decode_split_kernel<D, false, false>);
-  void* args[] = {const_cast<DecodeArgs*>(&a)};
-  if (C::LDS_BYTES > 65536) {
-    hipError_t e = hipFuncSetAttribute(f1, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
+  const dim3 grid1(a.Hkv * a.row_blocks, a.splits, a.B);   // splits = sub-chunks of all chunks
+  (void)hipGetLastError();   // start from a clean error state
+  if (bf16) {
+    if (causal) fa_decode_split_kernel<D, true, true><<<grid1, 64, 0, stream>>>(a);
+    else fa_decode_split_kernel<D, true, false><<<grid1, 64, 0, stream>>>(a);
+  } else {
+    if (causal) fa_decode_split_kernel<D, false, true><<<grid1, 64, 0, stream>>>(a);
+    else fa_decode_split_kernel<D, false, false><<<grid1, 64, 0, stream>>>(a);
   }
-  hipError_t e = hipLaunchKernel(f1, grid1, dim3(C::THREADS), args, C::LDS_BYTES, stream);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int RPB = 256 / (D / 4);
   const int rows = a.B * a.Hq * a.Nq;
   const dim3 grid2((rows + RPB - 1) / RPB);
-  const void* f2 = bf16 ? (const void*)fa_decode_combine_kernel<D, true> : (const void*)fa_decode_combine_kernel<D, false>;
-  return hipLaunchKernel(f2, grid2, dim3(256), args, 0, stream);
+  if (bf16) fa_decode_combine_kernel<D, true><<<grid2, 256, 0, stream>>>(a);
+  else fa_decode_combine_kernel<D, false><<<grid2, 256, 0, stream>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace fa

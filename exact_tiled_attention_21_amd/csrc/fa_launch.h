@@ -29,8 +29,10 @@ struct DecodeArgs {
   float* part_lse; // [S][B][Hq][Nq] float32, log2 domain
   int B, Nq, Nk, Hq, Hkv;
   int group;       // Hq / Hkv
-  int splits;      // S
-  int chunk;       // keys per split, a multiple of 32
+  int splits;      // partials per row: sub_per sub-chunks per requested chunk
+  int chunk;       // keys per requested chunk, a multiple of 32
+  int sub_per;     // sub-chunks per chunk: 1, 2 or 4
+  int sub;         // keys per sub-chunk, a multiple of 32
   int row_blocks;  // ceil(group * Nq / 32)
   float sl2;       // scale * log2(e)
 };

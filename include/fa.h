@@ -83,10 +83,11 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  fa_dtype dtype, void* stream);
 
 /*
- * Bytes of device workspace fa_decode_splitkv needs: float32 partial outputs
- * [num_splits][B][Hq][Nq][d] followed by float32 partial LSEs
- * [num_splits][B][Hq][Nq], each part padded to 256 bytes. Returns 0 for
- * invalid sizes.
+ * Bytes of device workspace fa_decode_splitkv needs. Each of the num_splits
+ * chunks is processed as up to 4 sub-chunks with a partial result each; the
+ * workspace holds float32 partial outputs [4*num_splits][B][Hq][Nq][d]
+ * followed by float32 partial LSEs [4*num_splits][B][Hq][Nq], each part
+ * padded to 256 bytes. Returns 0 for invalid sizes.
  */
 size_t fa_decode_workspace_bytes(int B, int Nq, int Hq, int d, int num_splits);
 
@@ -97,6 +98,10 @@ size_t fa_decode_workspace_bytes(int B, int Nq, int Hq, int d, int num_splits);
  *   num_splits : number of key chunks S, 1..FA_MAX_SPLITS. Chunk s covers keys
  *                [s*C, min(Nk, (s+1)*C)) with C = ceil(Nk/S) rounded up to a
  *                multiple of 32; chunks past Nk are empty and weigh nothing.
+ *                Each chunk is processed as P = 1, 2 or 4 sub-chunks of
+ *                ceil(C/P) keys (rounded up to 32), each by its own
+ *                workgroup; P grows when there are few chunks x heads x batch.
+ *                Nk * Hkv * d * 2 must stay below 2^31 (FA_ERR_SHAPE).
  *   causal     : as in fa_fwd (bottom-right aligned against Nk).
  *   workspace  : caller-owned device buffer of at least
  *                fa_decode_workspace_bytes(B, Nq, Hq, d, num_splits) bytes,

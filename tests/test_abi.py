@@ -69,8 +69,8 @@ def test_fwd_checks_nullptr_before_shape(lib):
 
 def test_workspace_size(lib):
     ws = lib.fa_decode_workspace_bytes
-    # [S][B][Hq][Nq][d] fp32 partial outputs, then [S][B][Hq][Nq] fp32 LSEs, each padded to 256 B
-    rows = 16 * 8 * 32 * 1
+    # [4S][B][Hq][Nq][d] fp32 partial outputs, then [4S][B][Hq][Nq] fp32 LSEs, each padded to 256 B
+    rows = 4 * 16 * 8 * 32 * 1
     assert ws(8, 1, 32, 128, 16) == rows * 128 * 4 + ((rows * 4 + 255) // 256) * 256
     assert ws(8, 1, 32, 128, 0) == 0
     assert ws(8, 1, 32, 100, 4) == 0
@@ -91,6 +91,7 @@ def dec(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, Nq=1, Nk=64, Hq=4, H
     (dict(Nk=0), 2), (dict(Hq=5, Hkv=2), 3), (dict(d=80), 4), (dict(dtype=7), 5),
     (dict(S=0), 6), (dict(S=_lib.FA_MAX_SPLITS + 1), 6),
     (dict(wsb=16), 7), (dict(ws=MIS), 9), (dict(k=MIS), 9), (dict(scale=float("-inf")), 10),
+    (dict(Nk=1 << 20, Hkv=8, Hq=8, d=256), 2),
 ])
 def test_decode_rejects_invalid_arguments(lib, kw, status):
     assert dec(lib, **kw) == status
