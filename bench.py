@@ -51,7 +51,21 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
-def time_steps(fn, steps, warmup, torch):
+def prewarm(fn, seconds, torch):
+    """Run fn for `seconds` of wall time before any counted step: the GPU raises
+    its clocks over the first tens of milliseconds of sustained load, and the
+    metric is the sustained rate."""
+    if seconds <= 0:
+        return
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_steps(fn, steps, warmup, torch, warm_s=0.0):
+    prewarm(fn, warm_s, torch)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -116,6 +130,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", choices=["fwd", "headline", "decode", "all"], default="all")
+    ap.add_argument("--prewarm-s", type=float, default=1.0,
+                    help="seconds of untimed launches per workload before its warmup steps")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -131,7 +147,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
     dev = torch.device("cuda:0")
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-              "higher_is_better": True, "scaling": "weak", "data": "synthetic"}
+              "higher_is_better": True, "scaling": "weak", "data": "synthetic",
+              "prewarm_s": args.prewarm_s}
 
     # ---- forward, headline workload (the line's value)
     w = synthetic.WORKLOADS["headline_f16_1024"]
@@ -147,7 +164,7 @@ def main():
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
         ms = time_steps(lambda i=0: attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse),
-                        args.steps, args.warmup, torch)
+                        args.steps, args.warmup, torch, args.prewarm_s)
         tflops = w.flops() / (ms * 1e-3) / 1e12
         traffic = measured_traffic()
         result.update({
@@ -171,7 +188,7 @@ def main():
         q, k, v = upload(w4, torch)
         o = torch.empty_like(q)
         ms4 = time_steps(lambda i=0: attention(q, k, v, scale=w4.scale, out=o), max(5, args.steps // 5),
-                         max(2, args.warmup // 5), torch)
+                         max(2, args.warmup // 5), torch, args.prewarm_s)
         t4 = w4.flops() / (ms4 * 1e-3) / 1e12
         result["fwd_4096"] = {"workload": w4.name, "ms": round(ms4, 4), "tflops": round(t4, 2),
                               "tflops_pages_convention": round(t4 / 2, 2),
@@ -196,7 +213,7 @@ def main():
             qq, kk, vv = sets[i % len(sets)]
             decode(qq, kk, vv, num_splits=wd.num_splits, scale=wd.scale, workspace=ws, out=o, lse=lse)
 
-        msd = time_steps(dstep, max(args.steps, 100), args.warmup, torch)
+        msd = time_steps(dstep, max(args.steps, 100), args.warmup, torch, args.prewarm_s)
         kv_bytes = 2 * wd.B * wd.Nk * wd.Hkv * wd.d * 2
         result["decode"] = {"workload": wd.name, "us_per_step": round(msd * 1e3, 2),
                             "kv_GBps": round(kv_bytes / (msd * 1e-3) / 1e9, 1),

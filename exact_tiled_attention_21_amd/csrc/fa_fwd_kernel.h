@@ -71,7 +71,7 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
   const FwdArgs& a;
   int lane, wave, hh, ln32;
   int qrow, q0w, diag;
-  int ntiles, nt_w, jmask;
+  int ntiles, nt_w, jmask, jfull;
   float sl2;
   V8 qf[C::NS];
   f32x16 oacc[C::NCB];
@@ -120,6 +120,13 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
     // first tile that needs an element mask for this wave (key tail or causal diagonal)
     jmask = (a.Nk % C::BC) ? a.Nk / C::BC : ntiles + 1;
     if (CAUSAL) jmask = min(jmask, max(0, (q0w + diag + 1) / C::BC));
+    // tiles before jfull need no mask and are computed by every wave of the
+    // workgroup (wave 0 has the fewest visible keys)
+    jfull = (a.Nk % C::BC) ? a.Nk / C::BC : ntiles;
+    const int q0 = qt * C::BR;
+    if (CAUSAL) jfull = min(jfull, max(0, (q0 + diag + 1) / C::BC));
+    if (q0 + C::BR > a.Nq) jfull = 0;   // a wave of this workgroup has no rows
+    jfull = min(jfull, ntiles);
 
     // HBM -> LDS by DMA through buffer resources (rows >= Nk read as 0). DMA piece
     // i of this wave fills LDS bytes [(i * NW + wave) * 1024, +1024): lane l writes
@@ -264,49 +271,58 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
     l_part += (psum[0] + psum[1]) + (psum[2] + psum[3]);
   }
 
-  // O += V_j P_j, with the transposing reads of V one MFMA ahead
+  // O += V_j P_j, with the transposing reads of V kVPre MFMAs ahead through a
+  // rolling buffer (slot i % (kVPre + 1) is refilled right after MFMA i used it)
   static constexpr int kPvMf = C::NT * C::NCB;
+  static constexpr int kVPre = 1;
   __device__ __forceinline__ void pv(const char* vt, const PF& pf) {
-    V8 vf[2];
-    vf[0] = vfrag(vt, 0, 0);
+    constexpr int NB = kVPre + 1;
+    V8 vf[NB];
+#pragma unroll
+    for (int i = 0; i < NB && i < kPvMf; ++i) vf[i] = vfrag(vt, i % C::NCB, i / C::NCB);
 #pragma unroll
     for (int i = 0; i < kPvMf; ++i) {
-      if (i + 1 < kPvMf) vf[(i + 1) & 1] = vfrag(vt, (i + 1) % C::NCB, (i + 1) / C::NCB);
-      oacc[i % C::NCB] = E::mfma(vf[i & 1], pf[i / C::NCB], oacc[i % C::NCB]);
+      oacc[i % C::NCB] = E::mfma(vf[i % NB], pf[i / C::NCB], oacc[i % C::NCB]);
+      if (i + NB < kPvMf) vf[i % NB] = vfrag(vt, (i + NB) % C::NCB, (i + NB) / C::NCB);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NB, 0);
 #pragma unroll
     for (int i = 0; i < kPvMf; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i + 2 < kPvMf) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-  }
-
-  // Finish tile jt: mask, max, reference update, probabilities.
-  __device__ __forceinline__ void softmax(SA& sacc, PF& pf, int jt) {
-    if (jt >= jmask) {
-      rebase(rowmax<true>(sacc, jt));
-      probs<true>(sacc, pf);
-    } else {
-      rebase(rowmax<false>(sacc, jt));
-      probs<false>(sacc, pf);
+      if (i + NB < kPvMf) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   }
 
   // One step over tile j (stage ST); the DMA started here fills tile j+1 into
-  // stage ST^1, which was last read in step j-1.
-  template <int ST>
+  // stage ST^1, which was last read in step j-1. TAIL steps cover the tiles
+  // where some wave of the workgroup needs an element mask (key tail, causal
+  // diagonal) or has no visible key; the other steps are straight-line code so
+  // the O accumulators keep their registers across the loop.
+  template <int ST, bool TAIL>
   __device__ __forceinline__ void step(int j, const FwdLds<D>& lds) {
     asm volatile("" : "+v"(kxo), "+v"(vx0), "+v"(vx1));
     if (j + 1 < ntiles) {
       dma(kg, j + 1, lds.k[ST ^ 1]);
       dma(vg, j + 1, lds.v[ST ^ 1]);
     }
-    if (j < nt_w) {
+    if (!TAIL) {
       SA sacc;
       PF pf;
       qk(lds.k[ST], sacc);
-      softmax(sacc, pf, j);
+      rebase(rowmax<false>(sacc, j));
+      probs<false>(sacc, pf);
+      pv(lds.v[ST], pf);
+    } else if (j < nt_w) {
+      SA sacc;
+      PF pf;
+      qk(lds.k[ST], sacc);
+      if (j >= jmask) {
+        rebase(rowmax<true>(sacc, j));
+        probs<true>(sacc, pf);
+      } else {
+        rebase(rowmax<false>(sacc, j));
+        probs<false>(sacc, pf);
+      }
       pv(lds.v[ST], pf);
     }
     __syncthreads();
@@ -360,10 +376,14 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fa_fwd
     w.dma(w.vg, 0, lds.v[0]);
   }
   __syncthreads();
-  for (int j = 0; j < w.ntiles; j += 2) {
-    w.template step<0>(j, lds);
-    if (j + 1 >= w.ntiles) break;
-    w.template step<1>(j + 1, lds);
+  int j = 0;
+  for (; j + 2 <= w.jfull; j += 2) {
+    w.template step<0, false>(j, lds);
+    w.template step<1, false>(j + 1, lds);
+  }
+  for (; j < w.ntiles; ++j) {
+    if (j & 1) w.template step<1, true>(j, lds);
+    else w.template step<0, true>(j, lds);
   }
   w.finish(b, hq);
 }
