@@ -220,6 +220,26 @@ def main():
                             "hbm_peak_frac": round(kv_bytes / (msd * 1e-3) / 1e9 / PEAK_HBM, 4),
                             "roofline_us": round(kv_bytes / (PEAK_HBM * 1e9) * 1e6, 2),
                             "kv_sets_rotated": len(sets)}
+        # the same step over a paged cache: 256-key pages in a scrambled block table
+        from exact_tiled_attention_21_amd import decode_paged
+        ps, mp = 256, wd.Nk // 256
+        bt = torch.from_numpy(synthetic.block_table(wd.wid, wd.B, mp, wd.B * mp)).to(dev)
+        lens = torch.full((wd.B,), wd.Nk, dtype=torch.int32, device=dev)
+        # each KV set seen as a pool of B * Nk / 256 pages; the scrambled table makes every
+        # sequence read pages scattered over the pool
+        pools = [(qq, kk.view(wd.B * mp, ps, wd.Hkv, wd.d), vv.view(wd.B * mp, ps, wd.Hkv, wd.d))
+                 for qq, kk, vv in sets]
+
+        def pstep(i=0):
+            qq, kk, vv = pools[i % len(pools)]
+            decode_paged(qq, kk, vv, bt, lens, num_splits=wd.num_splits, scale=wd.scale, workspace=ws,
+                         out=o, lse=lse)
+
+        msp = time_steps(pstep, max(args.steps, 100), args.warmup, torch, args.prewarm_s)
+        result["decode_paged"] = {"workload": wd.name, "page_size": ps, "us_per_step": round(msp * 1e3, 2),
+                                  "kv_GBps": round(kv_bytes / (msp * 1e-3) / 1e9, 1),
+                                  "hbm_peak_frac": round(kv_bytes / (msp * 1e-3) / 1e9 / PEAK_HBM, 4)}
+        del pools
         if "value" not in result:
             result.update({"value": round(msd * 1e3, 2), "unit": "us/step", "higher_is_better": False,
                            "ms_per_step": round(msd, 5), "vs_baseline": None, "dtype": "bf16",

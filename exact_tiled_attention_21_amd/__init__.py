@@ -5,6 +5,8 @@ kernels of libfa.so. torch supplies device memory and the current stream.
 
   attention(q, k, v, causal=False, scale=None) -> (o, lse)
   decode(q, k_cache, v_cache, num_splits=16, scale=None, causal=False) -> (o, lse)
+  decode_paged(q, k_pages, v_pages, block_table, cache_seqlens, num_splits=16,
+               scale=None, causal=False) -> (o, lse)
 
 Tensors are [batch, seq_len, heads, head_dim], fp16 or bf16, contiguous, on a
 ROCm device; lse is float32 [batch, heads, seq_len_q]. The default scale is
@@ -17,7 +19,7 @@ import math
 
 from ._lib import FA_BF16, FA_F16, FA_MAX_SPLITS, FaError, load, status_str  # noqa: F401
 
-__all__ = ["attention", "decode", "decode_workspace_bytes", "FaError", "load"]
+__all__ = ["attention", "decode", "decode_paged", "decode_workspace_bytes", "FaError", "load"]
 
 
 def _torch():
@@ -102,4 +104,44 @@ def decode(q, k_cache, v_cache, num_splits: int = 16, scale: float | None = None
                                       _stream(q))
     if st != 0:
         raise FaError(st, "fa_decode_splitkv")
+    return o, lse_t
+
+
+def decode_paged(q, k_pages, v_pages, block_table, cache_seqlens, num_splits: int = 16,
+                 scale: float | None = None, causal: bool = False, workspace=None, out=None, lse=None):
+    """Split-KV attention over a paged KV cache.
+
+    k_pages, v_pages: [num_pages, page_size, Hkv, d] page pools; block_table: int32
+    [B, max_pages_per_seq] page indices per sequence; cache_seqlens: int32 [B] keys
+    per sequence. page_size must be a multiple of 32."""
+    torch = _torch()
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages)):
+        if not t.is_cuda or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-d device tensor")
+    if not (q.dtype == k_pages.dtype == v_pages.dtype):
+        raise TypeError("q, k_pages, v_pages must share a dtype")
+    if k_pages.shape != v_pages.shape or q.shape[3] != k_pages.shape[3]:
+        raise ValueError("k_pages and v_pages must match, and share head_dim with q")
+    for name, t in (("block_table", block_table), ("cache_seqlens", cache_seqlens)):
+        if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    B, Nq, Hq, d = q.shape
+    num_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(cache_seqlens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_pages_per_seq] and cache_seqlens [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_bytes(B, Nq, Hq, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    with torch.cuda.device(q.device):
+        st = load().fa_decode_splitkv_paged(
+            q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+            cache_seqlens.data_ptr(), o.data_ptr(), lse_t.data_ptr(), B, Nq, Hq, Hkv, d, num_pages,
+            page_size, block_table.shape[1], int(num_splits), int(bool(causal)), float(scale),
+            _dtype_code(q), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_decode_splitkv_paged")
     return o, lse_t

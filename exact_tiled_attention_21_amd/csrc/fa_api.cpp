@@ -78,9 +78,28 @@ constexpr int kSubPerChunk = 4;
 // single-wave workgroups that give the chip about one round (256 CUs x 4 SIMDs)
 constexpr int64_t kDecodeWaves = 1024;
 
-int decode_chunk(int Nk, int splits) {
-  const int per = (Nk + splits - 1) / splits;
-  return (per + 31) / 32 * 32;
+// Fills the rest of the decode arguments (cache fields already set), checks the
+// grid limits and enqueues the split and combine kernels.
+fa_status launch_decode_common(fa::DecodeArgs& a, const void* q, void* o, float* lse, int B, int Nq,
+                               int Hq, int Hkv, int d, int num_splits, int causal, float scale,
+                               fa_dtype dtype, void* workspace, void* stream) {
+  const int group = Hq / Hkv;
+  const int64_t row_blocks = (int64_t(group) * Nq + 31) / 32;
+  if (int64_t(kSubPerChunk) * num_splits > 65535 || B > 65535) return FA_ERR_SHAPE;  // grid y / z limits
+  if (row_blocks * Hkv > 0x7fffffffLL) return FA_ERR_SHAPE;
+  a.q = q; a.o = o; a.lse = lse;
+  const size_t rows = size_t(kSubPerChunk) * num_splits * B * Hq * Nq;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pad256(rows * d * sizeof(float)));
+  a.B = B; a.Nq = Nq; a.Hq = Hq; a.Hkv = Hkv;
+  a.group = group;
+  const int64_t units = int64_t(num_splits) * Hkv * row_blocks * B;
+  a.sub_per = units >= kDecodeWaves ? 1 : (2 * units >= kDecodeWaves ? 2 : kSubPerChunk);
+  a.splits = a.sub_per * num_splits;
+  a.row_blocks = static_cast<int>(row_blocks);
+  a.sl2 = scale * 1.4426950408889634f;
+  hipError_t e = fa::launch_decode(a, d, dtype == FA_BF16, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -123,27 +142,46 @@ fa_status fa_decode_splitkv(const void* q, const void* k_cache, const void* v_ca
   const size_t need = fa_decode_workspace_bytes(B, Nq, Hq, d, num_splits);
   if (workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
-  const int group = Hq / Hkv;
-  const int64_t row_blocks = (int64_t(group) * Nq + 31) / 32;
-  if (int64_t(kSubPerChunk) * num_splits > 65535 || B > 65535) return FA_ERR_SHAPE;  // grid y / z limits
-  if (row_blocks * Hkv > 0x7fffffffLL) return FA_ERR_SHAPE;
   if (int64_t(Nk) * Hkv * d * 2 > 0x7fffffffLL) return FA_ERR_SHAPE;   // 32-bit buffer offsets
   fa::DecodeArgs a;
-  a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse;
-  const size_t rows = size_t(kSubPerChunk) * num_splits * B * Hq * Nq;
-  a.part_o = static_cast<float*>(workspace);
-  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pad256(rows * d * sizeof(float)));
-  a.B = B; a.Nq = Nq; a.Nk = Nk; a.Hq = Hq; a.Hkv = Hkv;
-  a.group = group;
-  const int64_t units = int64_t(num_splits) * Hkv * row_blocks * B;
-  a.sub_per = units >= kDecodeWaves ? 1 : (2 * units >= kDecodeWaves ? 2 : kSubPerChunk);
-  a.splits = a.sub_per * num_splits;
-  a.chunk = decode_chunk(Nk, num_splits);
-  a.sub = (((a.chunk + a.sub_per - 1) / a.sub_per) + 31) / 32 * 32;
-  a.row_blocks = static_cast<int>(row_blocks);
-  a.sl2 = scale * 1.4426950408889634f;
-  hipError_t e = fa::launch_decode(a, d, dtype == FA_BF16, causal != 0, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  a.k = k_cache; a.v = v_cache;
+  a.Nk = Nk;
+  a.block_table = nullptr; a.seqlens = nullptr;
+  a.page_size = 0; a.max_pages = 0; a.num_pages = 0;
+  return launch_decode_common(a, q, o, lse, B, Nq, Hq, Hkv, d, num_splits, causal, scale, dtype,
+                              workspace, stream);
+}
+
+fa_status fa_decode_splitkv_paged(const void* q, const void* k_pages, const void* v_pages,
+                                  const int* block_table, const int* cache_seqlens, void* o,
+                                  float* lse, int B, int Nq, int Hq, int Hkv, int d, int num_pages,
+                                  int page_size, int max_pages_per_seq, int num_splits, int causal,
+                                  float scale, fa_dtype dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!block_table || !cache_seqlens) return FA_ERR_NULLPTR;
+  if (num_pages < 1 || page_size < 32 || page_size % 32 != 0 || max_pages_per_seq < 1)
+    return FA_ERR_SHAPE;
+  const int64_t max_keys = int64_t(max_pages_per_seq) * page_size;
+  if (max_keys > 0x7fffffffLL) return FA_ERR_SHAPE;
+  // the common checks, with the pool standing in for the cache ([1][pool rows][Hkv][d])
+  const int64_t pool_rows = int64_t(num_pages) * page_size;
+  if (pool_rows > 0x7fffffffLL) return FA_ERR_SHAPE;
+  fa_status st = check_common(q, k_pages, v_pages, o, lse, B, Nq, static_cast<int>(pool_rows), Hq, Hkv,
+                              d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!workspace) return FA_ERR_NULLPTR;
+  if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
+  if (workspace_bytes < fa_decode_workspace_bytes(B, Nq, Hq, d, num_splits)) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(cache_seqlens) & 3u))
+    return FA_ERR_ALIGN;
+  fa::DecodeArgs a;
+  a.k = k_pages; a.v = v_pages;
+  a.Nk = static_cast<int>(max_keys);
+  a.block_table = block_table; a.seqlens = cache_seqlens;
+  a.page_size = page_size; a.max_pages = max_pages_per_seq; a.num_pages = num_pages;
+  return launch_decode_common(a, q, o, lse, B, Nq, Hq, Hkv, d, num_splits, causal, scale, dtype,
+                              workspace, stream);
 }
 
 const char* fa_status_str(fa_status s) {

@@ -19,6 +19,13 @@
 // sub-chunk partials of every chunk with the other chunks'. No barriers: up to
 // four such waves share a CU, one per SIMD.
 //
+// Paged cache ("flash-attention-v100" README, flash_attn_with_kvcache: a block
+// table maps each sequence's logical key blocks to pages of a shared pool, and
+// cache_seqlens gives each sequence's length): a 32-key tile never straddles a
+// page (the page size is a multiple of 32), so each tile costs one block-table
+// read and otherwise loads exactly like a contiguous tile. Chunks are cut per
+// sequence from its own length, and the causal mask is aligned to it.
+//
 // Combine kernel: per output row, LSE = log sum_s exp(LSE_s) and
 // O = sum_s exp(LSE_s - LSE) O_s; chunks with LSE_s = -inf weigh nothing.
 #pragma once
@@ -39,7 +46,7 @@ template <int D> struct DecCfg {
 };
 
 // One wave per workgroup: it streams the keys of one sub-chunk.
-template <int D, bool BF16, bool CAUSAL> struct DecWave {
+template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
   using C = DecCfg<D>;
   using E = Elem<BF16>;
   using T = typename E::T;
@@ -49,6 +56,7 @@ template <int D, bool BF16, bool CAUSAL> struct DecWave {
   const DecodeArgs& a;
   int lane, hh;
   bool rvalid;
+  int b, g, L;                  // batch, KV head, keys of this sequence
   int ri, rhq, diag, i_first, k_lo, k_hi, ntile;
   float sl2;
   V8 qf[C::NS];
@@ -61,11 +69,14 @@ template <int D, bool BF16, bool CAUSAL> struct DecWave {
   uint32_t goff;                // this lane's first 16-byte piece of a tile (coalesced rows)
   uint32_t kro, kxo, vb0, vb1, vx0, vx1;   // LDS fragment read offsets
 
-  __device__ __forceinline__ DecWave(const DecodeArgs& args, int part, int g, int rb, int b) : a(args) {
+  __device__ __forceinline__ DecWave(const DecodeArgs& args, int part, int g_, int rb, int b_)
+      : a(args), b(b_), g(g_) {
     lane = threadIdx.x & 63;
     hh = lane >> 5;
     const int R = a.group * a.Nq;               // rows of this KV head group
-    diag = a.Nk - a.Nq;
+    L = a.Nk;
+    if (PAGED) L = min(max(a.seqlens[b], 0), a.max_pages * a.page_size);
+    diag = L - a.Nq;
     // row r = i * group + (hq - g * group): consecutive rows are adjacent heads
     const int r = rb * 32 + (lane & 31);
     rvalid = r < R;
@@ -77,12 +88,17 @@ template <int D, bool BF16, bool CAUSAL> struct DecWave {
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) qf[s] = rvalid ? *reinterpret_cast<const V8*>(qp + 16 * s) : V8{};
 
-    // keys of this sub-chunk: chunk part / sub_per, piece part % sub_per; clipped
-    // by the chunk, the cache length and (causal) the last row
-    const int c_lo = (part / a.sub_per) * a.chunk;
-    const int c_hi = min(a.Nk, c_lo + a.chunk);
-    k_lo = c_lo + (part % a.sub_per) * a.sub;
-    k_hi = min(c_hi, k_lo + a.sub);
+    // keys of this sub-chunk: chunk part / sub_per, piece part % sub_per; chunks
+    // of ceil(L / S) keys and sub-chunks of ceil(chunk / sub_per) keys, both
+    // rounded up to 32; clipped by the chunk, the sequence length and (causal)
+    // the last row
+    const int S = a.splits / a.sub_per;
+    const int chunk = ((L + S - 1) / S + 31) / 32 * 32;
+    const int sub = ((chunk + a.sub_per - 1) / a.sub_per + 31) / 32 * 32;
+    const int c_lo = (part / a.sub_per) * chunk;
+    const int c_hi = min(L, c_lo + chunk);
+    k_lo = c_lo + (part % a.sub_per) * sub;
+    k_hi = min(c_hi, k_lo + sub);
     i_first = (rb * 32) / a.group;
     if (CAUSAL) {
       const int i_last = (min(R, rb * 32 + 32) - 1) / a.group;
@@ -91,7 +107,7 @@ template <int D, bool BF16, bool CAUSAL> struct DecWave {
     ntile = k_hi > k_lo ? (k_hi - k_lo + C::BC - 1) / C::BC : 0;
 
     rowbytes = static_cast<uint32_t>(a.Hkv) * D * 2;
-    const size_t head_off = (static_cast<size_t>(b) * a.Nk * a.Hkv + g) * D * 2;
+    const size_t head_off = ((PAGED ? 0 : static_cast<size_t>(b) * a.Nk * a.Hkv) + g) * D * 2;
     kg = reinterpret_cast<const char*>(a.k) + head_off;
     vg = reinterpret_cast<const char*>(a.v) + head_off;
     valid = static_cast<int64_t>(a.Nk - 1) * rowbytes + D * 2;
@@ -114,15 +130,29 @@ template <int D, bool BF16, bool CAUSAL> struct DecWave {
   }
 
   // K and V rows of tile t into registers, 16 lanes per 256-byte row (coalesced);
-  // rows past the cache read as zero through the buffer bounds check
+  // rows past the sequence read as zero through the buffer bounds check. A
+  // paged tile lies in one page; a page index outside the pool reads as zeros
+  // rather than leaving the pool.
   __device__ __forceinline__ void load(int t, Stage& ks, Stage& vs) const {
-    const int64_t off = static_cast<int64_t>(k_lo + t * C::BC) * rowbytes;
-    const int64_t rem = valid - off;
+    const int key0 = k_lo + t * C::BC;
+    int64_t off, rem;
+    if (PAGED) {
+      const int rows = min(C::BC, L - key0);
+      int page = -1;
+      if (rows > 0) page = a.block_table[static_cast<size_t>(b) * a.max_pages + key0 / a.page_size];
+      const bool ok = rows > 0 && page >= 0 && page < a.num_pages;
+      off = ok ? (static_cast<int64_t>(page) * a.page_size + key0 % a.page_size) * rowbytes : 0;
+      rem = ok ? static_cast<int64_t>(rows - 1) * rowbytes + D * 2 : 0;
+    } else {
+      off = static_cast<int64_t>(key0) * rowbytes;
+      rem = valid - off;
+      if (rem <= 0) off = 0;
+    }
     const uint32_t nrec = rem > 0 ? static_cast<uint32_t>(rem > 0x7fffffff ? 0x7fffffff : rem) : 0u;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(kg + (rem > 0 ? off : 0)), 0, nrec, 0x00020000);
+        const_cast<char*>(kg + off), 0, nrec, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(vg + (rem > 0 ? off : 0)), 0, nrec, 0x00020000);
+        const_cast<char*>(vg + off), 0, nrec, 0x00020000);
 #pragma unroll
     for (int i = 0; i < C::NCH; ++i) {
       const uint32_t o = goff_of(i);
@@ -219,10 +249,10 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(64) void fa_decode_split_kernel(const DecodeArgs a) {
   using C = DecCfg<D>;
-  using W = DecWave<D, BF16, CAUSAL>;
+  using W = DecWave<D, BF16, CAUSAL, PAGED>;
   __shared__ __attribute__((aligned(1024))) char kt[C::TILE];
   __shared__ __attribute__((aligned(1024))) char vt[C::TILE];
 
@@ -335,13 +365,20 @@ template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, bool bf16, bool causal, hipStream_t stream) {
   const dim3 grid1(a.Hkv * a.row_blocks, a.splits, a.B);   // splits = sub-chunks of all chunks
   (void)hipGetLastError();   // start from a clean error state
+  const bool paged = a.block_table != nullptr;
+#define FA_DEC_SPLIT(BF, CA)                                                     \
+  do {                                                                           \
+    if (paged) fa_decode_split_kernel<D, BF, CA, true><<<grid1, 64, 0, stream>>>(a); \
+    else fa_decode_split_kernel<D, BF, CA, false><<<grid1, 64, 0, stream>>>(a);      \
+  } while (0)
   if (bf16) {
-    if (causal) fa_decode_split_kernel<D, true, true><<<grid1, 64, 0, stream>>>(a);
-    else fa_decode_split_kernel<D, true, false><<<grid1, 64, 0, stream>>>(a);
+    if (causal) FA_DEC_SPLIT(true, true);
+    else FA_DEC_SPLIT(true, false);
   } else {
-    if (causal) fa_decode_split_kernel<D, false, true><<<grid1, 64, 0, stream>>>(a);
-    else fa_decode_split_kernel<D, false, false><<<grid1, 64, 0, stream>>>(a);
+    if (causal) FA_DEC_SPLIT(false, true);
+    else FA_DEC_SPLIT(false, false);
   }
+#undef FA_DEC_SPLIT
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int RPB = 256 / (D / 4);

@@ -30,11 +30,15 @@ struct DecodeArgs {
   int B, Nq, Nk, Hq, Hkv;
   int group;       // Hq / Hkv
   int splits;      // partials per row: sub_per sub-chunks per requested chunk
-  int chunk;       // keys per requested chunk, a multiple of 32
   int sub_per;     // sub-chunks per chunk: 1, 2 or 4
-  int sub;         // keys per sub-chunk, a multiple of 32
   int row_blocks;  // ceil(group * Nq / 32)
   float sl2;       // scale * log2(e)
+  // paged cache (block_table non-null): k and v point at page pools
+  // [num_pages][page_size][Hkv][d]; sequence b owns pages block_table[b][0..max_pages)
+  // and seqlens[b] keys. For a contiguous cache block_table and seqlens are null.
+  const int* block_table;
+  const int* seqlens;
+  int page_size, max_pages, num_pages;
 };
 
 // Rows of queries one forward workgroup covers (32 per wave).

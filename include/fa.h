@@ -114,6 +114,40 @@ fa_status fa_decode_splitkv(const void* q, const void* k_cache, const void* v_ca
                             int num_splits, int causal, float scale, fa_dtype dtype,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Split-KV attention over a paged KV cache with per-sequence lengths
+ * ("flash-attention-v100" README, How to use FlashAttention: the block_table and
+ * cache_seqlens arguments of flash_attn_with_kvcache).
+ *   q, o          : [B][Nq][Hq][d], `dtype`; lse: float32 [B][Hq][Nq] or NULL.
+ *   k_pages,
+ *   v_pages       : page pools [num_pages][page_size][Hkv][d], `dtype`.
+ *   block_table   : device int32 [B][max_pages_per_seq]; key j of sequence b
+ *                   lives in page block_table[b][j / page_size], row
+ *                   j % page_size. Entries past the sequence's last page are
+ *                   not read. An entry outside [0, num_pages) makes its keys
+ *                   read as zero vectors (results for that sequence are then
+ *                   undefined, but no memory outside the pools is touched).
+ *   cache_seqlens : device int32 [B]; sequence b has cache_seqlens[b] keys,
+ *                   clamped to [0, max_pages_per_seq * page_size]. A sequence
+ *                   with no key gets O = 0 and LSE = -inf.
+ *   page_size     : a multiple of 32 (>= 32).
+ *   num_splits    : as in fa_decode_splitkv, with C = ceil(len_b / S) rounded
+ *                   up to 32 computed per sequence from its own length.
+ *   causal        : bottom-right aligned against each sequence's length.
+ *   workspace     : fa_decode_workspace_bytes(B, Nq, Hq, d, num_splits) bytes.
+ * A contiguous cache [B][Nk][Hkv][d] with per-sequence lengths is the special
+ * case page_size = Nk (a multiple of 32), num_pages = B, block_table[b] = {b}.
+ * Status: FA_ERR_NULLPTR for a NULL block_table or cache_seqlens,
+ * FA_ERR_SHAPE for a bad page geometry, FA_ERR_ALIGN for a misaligned int32
+ * array, otherwise as fa_decode_splitkv.
+ */
+fa_status fa_decode_splitkv_paged(const void* q, const void* k_pages, const void* v_pages,
+                                  const int* block_table, const int* cache_seqlens, void* o,
+                                  float* lse, int B, int Nq, int Hq, int Hkv, int d, int num_pages,
+                                  int page_size, int max_pages_per_seq, int num_splits, int causal,
+                                  float scale, fa_dtype dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_str(fa_status status);
 

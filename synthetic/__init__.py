@@ -151,3 +151,12 @@ def _build():
 
 
 WORKLOADS = _build()
+
+
+def block_table(workload_id: int, B: int, max_pages: int, num_pages: int) -> np.ndarray:
+    """int32 [B, max_pages] page indices for a paged KV cache: a seeded permutation
+    of the pool's pages, so that no page is shared and logical order is scrambled."""
+    if num_pages < B * max_pages:
+        raise ValueError("the pool needs at least B * max_pages pages")
+    rng = np.random.default_rng([int(workload_id), 7])
+    return rng.permutation(num_pages)[: B * max_pages].astype(np.int32).reshape(B, max_pages)

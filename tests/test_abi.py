@@ -110,3 +110,24 @@ def test_no_oracle_on_product_path():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
                 assert "attention_f64" not in text, f
+
+
+def dec_paged(lib, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=FAKE, B=2, Nq=1, Hq=4, Hkv=2,
+              d=128, num_pages=8, page_size=64, max_pages=4, S=4, causal=0, scale=0.1, dtype=1,
+              ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = lib.fa_decode_workspace_bytes(B, Nq, Hq, d, S) if S >= 1 else 0
+    return lib.fa_decode_splitkv_paged(q, k, v, bt, sl, o, lse, B, Nq, Hq, Hkv, d, num_pages,
+                                       page_size, max_pages, S, causal, scale, dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bt=None), 1), (dict(sl=None), 1), (dict(q=None), 1), (dict(ws=None), 1),
+    (dict(page_size=48), 2), (dict(page_size=16), 2), (dict(page_size=0), 2), (dict(num_pages=0), 2),
+    (dict(max_pages=0), 2), (dict(page_size=1 << 20, max_pages=1 << 12), 2),
+    (dict(Hq=5), 3), (dict(d=80), 4), (dict(dtype=3), 5), (dict(S=0), 6), (dict(wsb=8), 7),
+    (dict(bt=FAKE + 2), 9), (dict(sl=FAKE + 1), 9), (dict(k=MIS), 9),
+    (dict(scale=float("nan")), 10),
+])
+def test_paged_decode_rejects_invalid_arguments(lib, kw, status):
+    assert dec_paged(lib, **kw) == status
