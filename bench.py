@@ -12,6 +12,7 @@ N=4096, each timed the same way. Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -140,6 +141,7 @@ def main():
               "(the sharding design is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
         return 2
 
+    import numpy as np
     import torch
     import synthetic
     from exact_tiled_attention_21_amd import attention, decode, decode_workspace_bytes
@@ -196,12 +198,30 @@ def main():
         del q, k, v, o
         torch.cuda.empty_cache()
 
+    if args.only in ("fwd", "all"):
+        # packed variable-length batch: 16 sequences of seeded lengths in [256, 2048],
+        # headline heads and head dim (FLOPs counted per sequence)
+        from exact_tiled_attention_21_amd import attention_varlen
+        rng = np.random.default_rng([w.wid, 99])
+        lens = rng.integers(256, 2049, size=16)
+        tot = int(lens.sum())
+        qv, kv_, vv_ = upload(dataclasses.replace(w, B=1, Nq=tot, Nk=tot), torch)
+        qv, kv_, vv_ = qv[0], kv_[0], vv_[0]
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+        ov = torch.empty_like(qv)
+        msv = time_steps(lambda i=0: attention_varlen(qv, kv_, vv_, cu, cu, int(lens.max()), scale=w.scale,
+                                                      out=ov), args.steps, args.warmup, torch, args.prewarm_s)
+        fl = float(sum(4.0 * w.Hq * int(n) * int(n) * w.d for n in lens))
+        result["fwd_varlen"] = {"workload": "16 packed sequences, lengths 256..2048 (seeded), Hq=Hkv=32, d=128, f16",
+                                "tokens": tot, "ms": round(msv, 4), "tflops": round(fl / (msv * 1e-3) / 1e12, 2)}
+        del qv, kv_, vv_, ov
+        torch.cuda.empty_cache()
+
     # ---- split-KV decode, rotating over KV sets larger than the 256 MB infinity cache
     if args.only in ("decode", "all"):
         wd = synthetic.WORKLOADS["decode_bf16_nq1"]
         sets = []
         for r in range(4):
-            import dataclasses
             wr = dataclasses.replace(wd, wid=wd.wid + 1000 * r)
             sets.append(upload(wr, torch))
         ws = torch.empty(decode_workspace_bytes(wd.B, wd.Nq, wd.Hq, wd.d, wd.num_splits), dtype=torch.uint8,

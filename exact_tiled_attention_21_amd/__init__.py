@@ -4,6 +4,8 @@ Argument marshalling only: every step of the computation runs in the HIP
 kernels of libfa.so. torch supplies device memory and the current stream.
 
   attention(q, k, v, causal=False, scale=None) -> (o, lse)
+  attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                   causal=False, scale=None) -> (o, lse)
   decode(q, k_cache, v_cache, num_splits=16, scale=None, causal=False) -> (o, lse)
   decode_paged(q, k_pages, v_pages, block_table, cache_seqlens, num_splits=16,
                scale=None, causal=False) -> (o, lse)
@@ -19,7 +21,7 @@ import math
 
 from ._lib import FA_BF16, FA_F16, FA_MAX_SPLITS, FaError, load, status_str  # noqa: F401
 
-__all__ = ["attention", "decode", "decode_paged", "decode_workspace_bytes", "FaError", "load"]
+__all__ = ["attention", "attention_varlen", "decode", "decode_paged", "decode_workspace_bytes", "FaError", "load"]
 
 
 def _torch():
@@ -144,4 +146,40 @@ def decode_paged(q, k_pages, v_pages, block_table, cache_seqlens, num_splits: in
             _dtype_code(q), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q))
     if st != 0:
         raise FaError(st, "fa_decode_splitkv_paged")
+    return o, lse_t
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
+                     scale: float | None = None, out=None, lse=None):
+    """Exact attention over a packed batch of variable-length sequences.
+
+    q [total_q, Hq, d], k/v [total_k, Hkv, d]; cu_seqlens_q/k int32 [B + 1] prefix
+    sums on the device; returns o like q and lse float32 [Hq, total_q]."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [tokens, heads, head_dim] device tensor")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if k.shape != v.shape or q.shape[2] != k.shape[2]:
+        raise ValueError("k and v must match, and share head_dim with q")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if not t.is_cuda or t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device vector")
+    if cu_seqlens_q.shape != cu_seqlens_k.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have B + 1 entries")
+    total_q, Hq, d = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.shape[0] - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    with torch.cuda.device(q.device):
+        st = load().fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(),
+                                  cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, int(max_seqlen_q),
+                                  total_q, total_k, Hq, Hkv, d, int(bool(causal)), float(scale),
+                                  _dtype_code(q), _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_fwd_varlen")
     return o, lse_t

@@ -118,6 +118,32 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   a.n_qtiles = (Nq + fa::fwd_rows(d) - 1) / fa::fwd_rows(d);
   a.sl2 = fabsf(scale) * 1.4426950408889634f;
   a.negate_q = scale < 0.f;
+  a.cu_q = nullptr; a.cu_k = nullptr; a.total_q = 0; a.total_k = 0;
+  const int64_t blocks = int64_t(a.n_qtiles) * Hq * B;
+  if (blocks > 0x7fffffff) return FA_ERR_SHAPE;
+  hipError_t e = fa::launch_fwd(a, d, dtype == FA_BF16, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int max_seqlen_q,
+                        int total_q, int total_k, int Hq, int Hkv, int d, int causal, float scale,
+                        fa_dtype dtype, void* stream) {
+  if (!cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULLPTR;
+  // the common checks, with the packed tensors as one batch element of total rows
+  fa_status st = check_common(q, k, v, o, lse, 1, total_q, total_k, Hq, Hkv, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (B < 1 || max_seqlen_q < 1) return FA_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return FA_ERR_ALIGN;
+  fa::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.Nq = max_seqlen_q; a.Nk = total_k; a.Hq = Hq; a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  a.n_qtiles = (max_seqlen_q + fa::fwd_rows(d) - 1) / fa::fwd_rows(d);
+  a.sl2 = fabsf(scale) * 1.4426950408889634f;
+  a.negate_q = scale < 0.f;
+  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k; a.total_q = total_q; a.total_k = total_k;
   const int64_t blocks = int64_t(a.n_qtiles) * Hq * B;
   if (blocks > 0x7fffffff) return FA_ERR_SHAPE;
   hipError_t e = fa::launch_fwd(a, d, dtype == FA_BF16, causal != 0, static_cast<hipStream_t>(stream));

@@ -51,6 +51,14 @@ template <int D> struct FwdCfg {
 
 constexpr float kLazy = 8.0f;   // log2 of the largest unnormalised probability kept
 
+// The sequence one workgroup works on: its query and key counts, the first
+// rows of its Q/O and K/V in the (padded or packed) tensors, and the index of
+// its first LSE entry.
+struct FwdSeq {
+  int nq, nk;
+  size_t q_row0, k_row0, lse0;
+};
+
 // LDS of one workgroup: two stages each for K and V, as separate objects so the
 // compiler knows a DMA into one stage never feeds a read of the other.
 template <int D> struct FwdLds {
@@ -69,6 +77,7 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
   typedef f32x16 SA[C::KB];
 
   const FwdArgs& a;
+  const FwdSeq& sq;
   int lane, wave, hh, ln32;
   int qrow, q0w, diag;
   int ntiles, nt_w, jmask, jfull;
@@ -85,7 +94,8 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
   // LDS read offsets
   uint32_t kro, kxo, vb0, vb1, vx0, vx1;
 
-  __device__ __forceinline__ FwdWave(const FwdArgs& args, int b, int hq, int g, int qt) : a(args) {
+  __device__ __forceinline__ FwdWave(const FwdArgs& args, const FwdSeq& seq, int hq, int g, int qt)
+      : a(args), sq(seq) {
     const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
@@ -93,39 +103,39 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
     ln32 = lane & 31;
     q0w = qt * C::BR + wave * 32;
     qrow = q0w + ln32;
-    diag = a.Nk - a.Nq;
+    diag = sq.nk - sq.nq;
     sl2 = a.sl2;
 
     // Q fragment (B operand): Q[qrow][16s + 8hh .. +7]; sign-flipped for a negative scale
     const T* qp = reinterpret_cast<const T*>(a.q) +
-                  ((static_cast<size_t>(b) * a.Nq + qrow) * a.Hq + hq) * D + 8 * hh;
+                  ((sq.q_row0 + qrow) * a.Hq + hq) * D + 8 * hh;
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) {
-      if (qrow < a.Nq) qf[s] = *reinterpret_cast<const V8*>(qp + 16 * s);
+      if (qrow < sq.nq) qf[s] = *reinterpret_cast<const V8*>(qp + 16 * s);
       else qf[s] = V8{};
       if (a.negate_q) qf[s] = -qf[s];
     }
 
     // key extents: the workgroup stages tiles up to kend; this wave computes up to wkend
-    int kend = a.Nk, wkend = a.Nk;
-    const int last_wg = min(qt * C::BR + C::BR, a.Nq) - 1;
-    const int last_w = min(q0w + 32, a.Nq) - 1;
+    int kend = sq.nk, wkend = sq.nk;
+    const int last_wg = min(qt * C::BR + C::BR, sq.nq) - 1;
+    const int last_w = min(q0w + 32, sq.nq) - 1;
     if (CAUSAL) {
-      kend = min(a.Nk, last_wg + diag + 1);
-      wkend = min(a.Nk, last_w + diag + 1);
+      kend = min(sq.nk, last_wg + diag + 1);
+      wkend = min(sq.nk, last_w + diag + 1);
     }
-    if (q0w >= a.Nq) wkend = 0;
+    if (q0w >= sq.nq) wkend = 0;
     ntiles = kend > 0 ? (kend + C::BC - 1) / C::BC : 0;
     nt_w = wkend > 0 ? (wkend + C::BC - 1) / C::BC : 0;
     // first tile that needs an element mask for this wave (key tail or causal diagonal)
-    jmask = (a.Nk % C::BC) ? a.Nk / C::BC : ntiles + 1;
+    jmask = (sq.nk % C::BC) ? sq.nk / C::BC : ntiles + 1;
     if (CAUSAL) jmask = min(jmask, max(0, (q0w + diag + 1) / C::BC));
     // tiles before jfull need no mask and are computed by every wave of the
     // workgroup (wave 0 has the fewest visible keys)
-    jfull = (a.Nk % C::BC) ? a.Nk / C::BC : ntiles;
+    jfull = (sq.nk % C::BC) ? sq.nk / C::BC : ntiles;
     const int q0 = qt * C::BR;
     if (CAUSAL) jfull = min(jfull, max(0, (q0 + diag + 1) / C::BC));
-    if (q0 + C::BR > a.Nq) jfull = 0;   // a wave of this workgroup has no rows
+    if (q0 + C::BR > sq.nq) jfull = 0;   // a wave of this workgroup has no rows
     jfull = min(jfull, ntiles);
 
     // HBM -> LDS by DMA through buffer resources (rows >= Nk read as 0). DMA piece
@@ -133,10 +143,10 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
     // 16 bytes at +16 l, i.e. physical chunk pch of row r, so it fetches logical
     // chunk pch ^ swz(r) of that row.
     rowbytes = static_cast<uint32_t>(a.Hkv) * D * 2;
-    const size_t head_off = (static_cast<size_t>(b) * a.Nk * a.Hkv + g) * D * 2;
+    const size_t head_off = (sq.k_row0 * a.Hkv + g) * D * 2;
     kg = reinterpret_cast<const char*>(a.k) + head_off;
     vg = reinterpret_cast<const char*>(a.v) + head_off;
-    valid = static_cast<int64_t>(a.Nk - 1) * rowbytes + D * 2;
+    valid = static_cast<int64_t>(sq.nk - 1) * rowbytes + D * 2;
 #pragma unroll
     for (int i = 0; i < C::NDMA; ++i) {
       const uint32_t p = (i * C::NW + wave) * 1024 + lane * 16;
@@ -223,7 +233,7 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key >= a.Nk || (CAUSAL && key > qrow + diag)) sacc[kb][r] = kNegInf;
+          if (key >= sq.nk || (CAUSAL && key > qrow + diag)) sacc[kb][r] = kNegInf;
         }
     }
     float mx = kNegInf;
@@ -329,11 +339,11 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
   }
 
   // O = O / l, LSE = m + log(l); rows with no visible key give 0 and -inf
-  __device__ __forceinline__ void finish(int b, int hq) {
+  __device__ __forceinline__ void finish(int hq) {
     const float l = halves_sum(l_part);
-    if (qrow >= a.Nq) return;
+    if (qrow >= sq.nq) return;
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    T* op = reinterpret_cast<T*>(a.o) + ((static_cast<size_t>(b) * a.Nq + qrow) * a.Hq + hq) * D;
+    T* op = reinterpret_cast<T*>(a.o) + ((sq.q_row0 + qrow) * a.Hq + hq) * D;
 #pragma unroll
     for (int cb = 0; cb < C::NCB; ++cb) {
 #pragma unroll
@@ -346,7 +356,7 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
       }
     }
     if (a.lse != nullptr && hh == 0)
-      a.lse[(static_cast<size_t>(b) * a.Hq + hq) * a.Nq + qrow] =
+      a.lse[sq.lse0 + qrow] =
           l > 0.f ? (m_run + __log2f(l)) * kLn2 : kNegInf;
   }
 };
@@ -369,7 +379,24 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fa_fwd
   if (CAUSAL) qt = a.n_qtiles - 1 - qt;  // longest rows first
   const int g = hq / a.group;
 
-  FwdWave<D, BF16, CAUSAL> w(a, b, hq, g, qt);
+  // the sequence: a padded batch element, or one packed sequence whose bounds
+  // come from the prefix sums (clamped into the tensors, so a malformed table
+  // cannot lead outside them); workgroups past its last query row have nothing to do
+  FwdSeq sq;
+  if (a.cu_q != nullptr) {
+    const int q_lo = min(max(a.cu_q[b], 0), a.total_q);
+    const int q_hi = min(max(a.cu_q[b + 1], q_lo), a.total_q);
+    const int k_lo = min(max(a.cu_k[b], 0), a.total_k);
+    const int k_hi = min(max(a.cu_k[b + 1], k_lo), a.total_k);
+    sq = FwdSeq{q_hi - q_lo, k_hi - k_lo, static_cast<size_t>(q_lo), static_cast<size_t>(k_lo),
+                static_cast<size_t>(hq) * a.total_q + q_lo};
+    if (qt * C::BR >= sq.nq) return;   // uniform over the workgroup, before any barrier
+  } else {
+    sq = FwdSeq{a.Nq, a.Nk, static_cast<size_t>(b) * a.Nq, static_cast<size_t>(b) * a.Nk,
+                (static_cast<size_t>(b) * a.Hq + hq) * a.Nq};
+  }
+
+  FwdWave<D, BF16, CAUSAL> w(a, sq, hq, g, qt);
   const FwdLds<D> lds{{k_lds0, k_lds1}, {v_lds0, v_lds1}};
   if (w.ntiles > 0) {
     w.dma(w.kg, 0, lds.k[0]);
@@ -385,7 +412,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fa_fwd
     if (j & 1) w.template step<1, true>(j, lds);
     else w.template step<0, true>(j, lds);
   }
-  w.finish(b, hq);
+  w.finish(hq);
 }
 
 template <int D>

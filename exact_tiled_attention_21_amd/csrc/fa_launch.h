@@ -17,6 +17,12 @@ struct FwdArgs {
   int n_qtiles;    // ceil(Nq / rows per workgroup)
   float sl2;       // |scale| * log2(e)
   int negate_q;    // scale < 0: the kernel flips the sign of Q instead
+  // packed variable-length batch (cu_q non-null): q/o are [total_q][Hq][d], k/v
+  // [total_k][Hkv][d], lse [Hq][total_q]; sequence b owns rows cu_q[b] ..
+  // cu_q[b+1] of q and cu_k[b] .. cu_k[b+1] of k; Nq is the longest query count
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
 };
 
 struct DecodeArgs {

@@ -83,6 +83,32 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  fa_dtype dtype, void* stream);
 
 /*
+ * Attention forward pass over a packed batch of variable-length sequences (the
+ * flash_attn_varlen_func entry point named in the "flash-attention-v100"
+ * README, Changelog 2.0; the argument reading is ours): sequence b owns query
+ * rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] ..
+ * cu_seqlens_k[b+1]-1, and attends only within itself.
+ *   q, o          : [total_q][Hq][d]; k, v: [total_k][Hkv][d]; all `dtype`.
+ *   lse           : float32 [Hq][total_q] or NULL.
+ *   cu_seqlens_q,
+ *   cu_seqlens_k  : device int32 [B + 1], non-decreasing prefix sums starting
+ *                   at 0 and ending at total_q / total_k. Values are clamped to
+ *                   [0, total]; a malformed table gives undefined results for
+ *                   the affected sequences but no access outside the tensors.
+ *   max_seqlen_q  : the longest query count (sizes the grid; rows beyond a
+ *                   sequence's own count are not computed).
+ *   causal        : bottom-right aligned per sequence, as in fa_fwd. A
+ *                   sequence with no key gets O = 0 and LSE = -inf.
+ * Status: FA_ERR_NULLPTR for a NULL prefix-sum array, FA_ERR_ALIGN for a
+ * misaligned one, FA_ERR_SHAPE for B or max_seqlen_q < 1 or totals < 1,
+ * otherwise as fa_fwd.
+ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int max_seqlen_q,
+                        int total_q, int total_k, int Hq, int Hkv, int d, int causal, float scale,
+                        fa_dtype dtype, void* stream);
+
+/*
  * Bytes of device workspace fa_decode_splitkv needs. Each of the num_splits
  * chunks is processed as up to 4 sub-chunks with a partial result each; the
  * workspace holds float32 partial outputs [4*num_splits][B][Hq][Nq][d]

@@ -131,3 +131,18 @@ def dec_paged(lib, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=FAKE, B
 ])
 def test_paged_decode_rejects_invalid_arguments(lib, kw, status):
     assert dec_paged(lib, **kw) == status
+
+
+def fwd_varlen(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cq=FAKE, ck=FAKE, B=2, max_q=8, tq=16, tk=16,
+               Hq=2, Hkv=1, d=64, causal=0, scale=0.125, dtype=0):
+    return lib.fa_fwd_varlen(q, k, v, o, lse, cq, ck, B, max_q, tq, tk, Hq, Hkv, d, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cq=None), 1), (dict(ck=None), 1), (dict(q=None), 1),
+    (dict(B=0), 2), (dict(max_q=0), 2), (dict(tq=0), 2), (dict(tk=0), 2),
+    (dict(Hq=3, Hkv=2), 3), (dict(d=40), 4), (dict(dtype=9), 5),
+    (dict(cq=FAKE + 2), 9), (dict(ck=FAKE + 1), 9), (dict(o=MIS), 9), (dict(scale=float("inf")), 10),
+])
+def test_fwd_varlen_rejects_invalid_arguments(lib, kw, status):
+    assert fwd_varlen(lib, **kw) == status
