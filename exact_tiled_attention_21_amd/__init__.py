@@ -61,8 +61,11 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def attention(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
-    """Exact attention forward: softmax(scale * q k^T [+ causal mask]) v, plus per-row LSE."""
+def attention(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+              window=(-1, -1)):
+    """Exact attention forward: softmax(scale * q k^T [+ causal mask or sliding-window
+    band]) v, plus per-row LSE. window = (left, right) keys around the bottom-right
+    aligned diagonal, -1 for an open side."""
     torch = _torch()
     _check(q, k, v)
     B, Nq, Hq, d = q.shape
@@ -72,9 +75,15 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
     with torch.cuda.device(q.device):
-        st = load().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(),
-                           B, Nq, Nk, Hq, Hkv, d, int(bool(causal)), float(scale), _dtype_code(q),
-                           _stream(q))
+        if tuple(window) == (-1, -1):
+            st = load().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(),
+                               B, Nq, Nk, Hq, Hkv, d, int(bool(causal)), float(scale), _dtype_code(q),
+                               _stream(q))
+        else:
+            st = load().fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                      lse_t.data_ptr(), B, Nq, Nk, Hq, Hkv, d, int(window[0]),
+                                      int(window[1]), int(bool(causal)), float(scale), _dtype_code(q),
+                                      _stream(q))
     if st != 0:
         raise FaError(st, "fa_fwd")
     return o, lse_t

@@ -11,7 +11,7 @@ FA_MAX_SPLITS = 256
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULLPTR", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADS", 4: "FA_ERR_HEADDIM",
           5: "FA_ERR_DTYPE", 6: "FA_ERR_SPLITS", 7: "FA_ERR_WORKSPACE", 8: "FA_ERR_LAUNCH",
           9: "FA_ERR_ALIGN", 10: "FA_ERR_SCALE"}
-EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_decode_splitkv_paged",
+EXPORTS = ("fa_fwd", "fa_fwd_window", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_splitkv", "fa_decode_splitkv_paged",
            "fa_status_str")
 
 _lib = None
@@ -35,6 +35,8 @@ def load(path: str = LIB_PATH):
     P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
     lib.fa_fwd.restype = I
+    lib.fa_fwd_window.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P]
+    lib.fa_fwd_window.restype = I
     lib.fa_fwd_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P]
     lib.fa_fwd_varlen.restype = I
     lib.fa_decode_workspace_bytes.argtypes = [I, I, I, I, I]

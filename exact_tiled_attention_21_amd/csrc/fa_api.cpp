@@ -20,14 +20,14 @@ hipError_t launch_decode_d128(const DecodeArgs&, bool, bool, hipStream_t);
 hipError_t launch_decode_d192(const DecodeArgs&, bool, bool, hipStream_t);
 hipError_t launch_decode_d256(const DecodeArgs&, bool, bool, hipStream_t);
 
-hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool causal, hipStream_t s) {
+hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool band, hipStream_t s) {
   switch (d) {
-    case 32: return launch_fwd_d32(a, bf16, causal, s);
-    case 64: return launch_fwd_d64(a, bf16, causal, s);
-    case 96: return launch_fwd_d96(a, bf16, causal, s);
-    case 128: return launch_fwd_d128(a, bf16, causal, s);
-    case 192: return launch_fwd_d192(a, bf16, causal, s);
-    case 256: return launch_fwd_d256(a, bf16, causal, s);
+    case 32: return launch_fwd_d32(a, bf16, band, s);
+    case 64: return launch_fwd_d64(a, bf16, band, s);
+    case 96: return launch_fwd_d96(a, bf16, band, s);
+    case 128: return launch_fwd_d128(a, bf16, band, s);
+    case 192: return launch_fwd_d192(a, bf16, band, s);
+    case 256: return launch_fwd_d256(a, bf16, band, s);
   }
   return hipErrorInvalidValue;
 }
@@ -102,6 +102,23 @@ fa_status launch_decode_common(fa::DecodeArgs& a, const void* q, void* o, float*
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// Fills the rest of the forward arguments (tensors and sizes already set) and
+// enqueues the kernel. Causal fixes the right edge of the band at the diagonal.
+fa_status fwd_common(fa::FwdArgs& a, int d, int wl, int wr, int causal, float scale, fa_dtype dtype,
+                     void* stream) {
+  a.group = a.Hq / a.Hkv;
+  a.n_qtiles = (a.Nq + fa::fwd_rows(d) - 1) / fa::fwd_rows(d);
+  a.sl2 = fabsf(scale) * 1.4426950408889634f;
+  a.negate_q = scale < 0.f;
+  a.wl = wl;
+  a.wr = causal ? 0 : wr;
+  const int64_t blocks = int64_t(a.n_qtiles) * a.Hq * a.B;
+  if (blocks > 0x7fffffff) return FA_ERR_SHAPE;
+  const bool band = a.wl >= 0 || a.wr >= 0;
+  hipError_t e = fa::launch_fwd(a, d, dtype == FA_BF16, band, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,20 +126,20 @@ extern "C" {
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int Nq, int Nk, int Hq, int Hkv, int d, int causal, float scale,
                  fa_dtype dtype, void* stream) {
+  return fa_fwd_window(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, -1, -1, causal, scale, dtype, stream);
+}
+
+fa_status fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Nq, int Nk, int Hq, int Hkv, int d, int window_left,
+                        int window_right, int causal, float scale, fa_dtype dtype, void* stream) {
   fa_status st = check_common(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, scale, dtype);
   if (st != FA_OK) return st;
+  if (window_left < -1 || window_right < -1) return FA_ERR_SHAPE;
   fa::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.B = B; a.Nq = Nq; a.Nk = Nk; a.Hq = Hq; a.Hkv = Hkv;
-  a.group = Hq / Hkv;
-  a.n_qtiles = (Nq + fa::fwd_rows(d) - 1) / fa::fwd_rows(d);
-  a.sl2 = fabsf(scale) * 1.4426950408889634f;
-  a.negate_q = scale < 0.f;
   a.cu_q = nullptr; a.cu_k = nullptr; a.total_q = 0; a.total_k = 0;
-  const int64_t blocks = int64_t(a.n_qtiles) * Hq * B;
-  if (blocks > 0x7fffffff) return FA_ERR_SHAPE;
-  hipError_t e = fa::launch_fwd(a, d, dtype == FA_BF16, causal != 0, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  return fwd_common(a, d, window_left, window_right, causal, scale, dtype, stream);
 }
 
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -139,15 +156,8 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
   fa::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.B = B; a.Nq = max_seqlen_q; a.Nk = total_k; a.Hq = Hq; a.Hkv = Hkv;
-  a.group = Hq / Hkv;
-  a.n_qtiles = (max_seqlen_q + fa::fwd_rows(d) - 1) / fa::fwd_rows(d);
-  a.sl2 = fabsf(scale) * 1.4426950408889634f;
-  a.negate_q = scale < 0.f;
   a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k; a.total_q = total_q; a.total_k = total_k;
-  const int64_t blocks = int64_t(a.n_qtiles) * Hq * B;
-  if (blocks > 0x7fffffff) return FA_ERR_SHAPE;
-  hipError_t e = fa::launch_fwd(a, d, dtype == FA_BF16, causal != 0, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  return fwd_common(a, d, -1, -1, causal, scale, dtype, stream);
 }
 
 size_t fa_decode_workspace_bytes(int B, int Nq, int Hq, int d, int num_splits) {

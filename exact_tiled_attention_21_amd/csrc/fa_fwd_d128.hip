@@ -2,7 +2,7 @@
 #include "fa_fwd_kernel.h"
 
 namespace fa {
-hipError_t launch_fwd_d128(const FwdArgs& a, bool bf16, bool causal, hipStream_t stream) {
-  return launch_fwd_d<128>(a, bf16, causal, stream);
+hipError_t launch_fwd_d128(const FwdArgs& a, bool bf16, bool band, hipStream_t stream) {
+  return launch_fwd_d<128>(a, bf16, band, stream);
 }
 }  // namespace fa

@@ -68,7 +68,7 @@ template <int D> struct FwdLds {
 };
 
 // Per-wave state and the steps of the tile loop (device code only).
-template <int D, bool BF16, bool CAUSAL> struct FwdWave {
+template <int D, bool BF16, bool BAND> struct FwdWave {
   using C = FwdCfg<D>;
   using E = Elem<BF16>;
   using T = typename E::T;
@@ -80,7 +80,10 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
   const FwdSeq& sq;
   int lane, wave, hh, ln32;
   int qrow, q0w, diag;
-  int ntiles, nt_w, jmask, jfull;
+  // tiles [jlo, jhi) hold a key some row of the workgroup sees; tiles
+  // [jua, jub) need no element mask for any row (the others are computed with it)
+  int jlo, jhi, jua, jub;
+  int lo_key, hi_key;   // keys this lane's row sees: lo_key <= key <= hi_key
   float sl2;
   V8 qf[C::NS];
   f32x16 oacc[C::NCB];
@@ -93,6 +96,14 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
   uint32_t goff[C::NDMA];
   // LDS read offsets
   uint32_t kro, kxo, vb0, vb1, vx0, vx1;
+
+  // first key row i sees, and one past its last (band and cache bounds)
+  __device__ __forceinline__ int lbound(int i) const {
+    return (BAND && a.wl >= 0) ? max(0, i + diag - a.wl) : 0;
+  }
+  __device__ __forceinline__ int rbound(int i) const {
+    return (BAND && a.wr >= 0) ? min(sq.nk, i + diag + a.wr + 1) : sq.nk;
+  }
 
   __device__ __forceinline__ FwdWave(const FwdArgs& args, const FwdSeq& seq, int hq, int g, int qt)
       : a(args), sq(seq) {
@@ -116,27 +127,24 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
       if (a.negate_q) qf[s] = -qf[s];
     }
 
-    // key extents: the workgroup stages tiles up to kend; this wave computes up to wkend
-    int kend = sq.nk, wkend = sq.nk;
-    const int last_wg = min(qt * C::BR + C::BR, sq.nq) - 1;
-    const int last_w = min(q0w + 32, sq.nq) - 1;
-    if (CAUSAL) {
-      kend = min(sq.nk, last_wg + diag + 1);
-      wkend = min(sq.nk, last_w + diag + 1);
-    }
-    if (q0w >= sq.nq) wkend = 0;
-    ntiles = kend > 0 ? (kend + C::BC - 1) / C::BC : 0;
-    nt_w = wkend > 0 ? (wkend + C::BC - 1) / C::BC : 0;
-    // first tile that needs an element mask for this wave (key tail or causal diagonal)
-    jmask = (sq.nk % C::BC) ? sq.nk / C::BC : ntiles + 1;
-    if (CAUSAL) jmask = min(jmask, max(0, (q0w + diag + 1) / C::BC));
-    // tiles before jfull need no mask and are computed by every wave of the
-    // workgroup (wave 0 has the fewest visible keys)
-    jfull = (sq.nk % C::BC) ? sq.nk / C::BC : ntiles;
+    // Key extents. Row i sees keys j with i + diag - wl <= j <= i + diag + wr
+    // (the band of a sliding window; causal is wl = none, wr = 0), clipped to
+    // [0, nk). The first row has the smallest bounds, the last the largest.
+    const int nk = sq.nk;
+    const bool has_l = BAND && a.wl >= 0, has_r = BAND && a.wr >= 0;
     const int q0 = qt * C::BR;
-    if (CAUSAL) jfull = min(jfull, max(0, (q0 + diag + 1) / C::BC));
-    if (q0 + C::BR > sq.nq) jfull = 0;   // a wave of this workgroup has no rows
-    jfull = min(jfull, ntiles);
+    const int last_wg = min(q0 + C::BR, sq.nq) - 1;
+    lo_key = has_l ? qrow + diag - a.wl : -0x7fffffff;
+    hi_key = min(nk, has_r ? qrow + diag + a.wr + 1 : nk) - 1;
+    // tiles of the workgroup
+    const int kb = lbound(q0), ke = rbound(last_wg);
+    jlo = kb / C::BC;
+    jhi = ke > kb ? (ke + C::BC - 1) / C::BC : jlo;
+    // tiles without element masks: inside every row's band and below nk
+    jua = max(jlo, has_l ? (lbound(last_wg) + C::BC - 1) / C::BC : 0);
+    jub = min(jhi, min(nk / C::BC, has_r ? max(0, rbound(q0)) / C::BC : nk / C::BC));
+    if (q0 + C::BR > sq.nq) jub = jua;   // a wave of this workgroup has no rows
+    if (jub < jua) jub = jua;
 
     // HBM -> LDS by DMA through buffer resources (rows >= Nk read as 0). DMA piece
     // i of this wave fills LDS bytes [(i * NW + wave) * 1024, +1024): lane l writes
@@ -233,7 +241,7 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key >= sq.nk || (CAUSAL && key > qrow + diag)) sacc[kb][r] = kNegInf;
+          if (key < lo_key || key > hi_key) sacc[kb][r] = kNegInf;
         }
     }
     float mx = kNegInf;
@@ -311,7 +319,7 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
   template <int ST, bool TAIL>
   __device__ __forceinline__ void step(int j, const FwdLds<D>& lds) {
     asm volatile("" : "+v"(kxo), "+v"(vx0), "+v"(vx1));
-    if (j + 1 < ntiles) {
+    if (j + 1 < jhi) {
       dma(kg, j + 1, lds.k[ST ^ 1]);
       dma(vg, j + 1, lds.v[ST ^ 1]);
     }
@@ -322,17 +330,15 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
       rebase(rowmax<false>(sacc, j));
       probs<false>(sacc, pf);
       pv(lds.v[ST], pf);
-    } else if (j < nt_w) {
+    } else {
+      // masked tiles: every wave computes them with the element mask, so the
+      // step stays straight-line code (a wave that sees none of the tile gets
+      // probabilities 0 from it)
       SA sacc;
       PF pf;
       qk(lds.k[ST], sacc);
-      if (j >= jmask) {
-        rebase(rowmax<true>(sacc, j));
-        probs<true>(sacc, pf);
-      } else {
-        rebase(rowmax<false>(sacc, j));
-        probs<false>(sacc, pf);
-      }
+      rebase(rowmax<true>(sacc, j));
+      probs<true>(sacc, pf);
       pv(lds.v[ST], pf);
     }
     __syncthreads();
@@ -361,7 +367,7 @@ template <int D, bool BF16, bool CAUSAL> struct FwdWave {
   }
 };
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool BAND>
 __global__ __launch_bounds__(FwdCfg<D>::THREADS)
 __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fa_fwd_kernel(const FwdArgs a) {
   using C = FwdCfg<D>;
@@ -376,7 +382,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fa_fwd
   const int hb = bid / a.n_qtiles;
   const int hq = hb % a.Hq;
   const int b = hb / a.Hq;
-  if (CAUSAL) qt = a.n_qtiles - 1 - qt;  // longest rows first
+  if (BAND) qt = a.n_qtiles - 1 - qt;  // with a causal band: longest rows first
   const int g = hq / a.group;
 
   // the sequence: a padded batch element, or one packed sequence whose bounds
@@ -396,36 +402,59 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fa_fwd
                 (static_cast<size_t>(b) * a.Hq + hq) * a.Nq};
   }
 
-  FwdWave<D, BF16, CAUSAL> w(a, sq, hq, g, qt);
+  FwdWave<D, BF16, BAND> w(a, sq, hq, g, qt);
   const FwdLds<D> lds{{k_lds0, k_lds1}, {v_lds0, v_lds1}};
-  if (w.ntiles > 0) {
-    w.dma(w.kg, 0, lds.k[0]);
-    w.dma(w.vg, 0, lds.v[0]);
+  // tile j lives in stage (j - jlo) & 1
+  if (w.jhi > w.jlo) {
+    w.dma(w.kg, w.jlo, lds.k[0]);
+    w.dma(w.vg, w.jlo, lds.v[0]);
   }
   __syncthreads();
-  int j = 0;
-  for (; j + 2 <= w.jfull; j += 2) {
+  int j = w.jlo;
+  // masked tiles before the unmasked run (the left edge of a band); all of
+  // them when there is no unmasked run
+  const int head_end = w.jub > w.jua ? w.jua : w.jhi;
+  for (; j + 2 <= head_end; j += 2) {   // j - jlo is even here
+    w.template step<0, true>(j, lds);
+    w.template step<1, true>(j + 1, lds);
+  }
+  if (j < head_end) {
+    w.template step<0, true>(j, lds);
+    ++j;
+  }
+  // the unmasked run, two tiles per iteration with compile-time stages
+  if (j < w.jub && ((j - w.jlo) & 1)) {
+    w.template step<1, false>(j, lds);
+    ++j;
+  }
+  for (; j + 2 <= w.jub; j += 2) {
     w.template step<0, false>(j, lds);
     w.template step<1, false>(j + 1, lds);
   }
-  for (; j < w.ntiles; ++j) {
-    if (j & 1) w.template step<1, true>(j, lds);
-    else w.template step<0, true>(j, lds);
+  // masked tiles after it (key tail, diagonal, right edge of a band)
+  if (j < w.jhi && ((j - w.jlo) & 1)) {
+    w.template step<1, true>(j, lds);
+    ++j;
   }
+  for (; j + 2 <= w.jhi; j += 2) {
+    w.template step<0, true>(j, lds);
+    w.template step<1, true>(j + 1, lds);
+  }
+  if (j < w.jhi) w.template step<0, true>(j, lds);
   w.finish(hq);
 }
 
 template <int D>
-hipError_t launch_fwd_d(const FwdArgs& a, bool bf16, bool causal, hipStream_t stream) {
+hipError_t launch_fwd_d(const FwdArgs& a, bool bf16, bool band, hipStream_t stream) {
   using C = FwdCfg<D>;
   const dim3 grid(static_cast<unsigned>(a.n_qtiles) * a.Hq * a.B);
   const dim3 block(C::THREADS);
   (void)hipGetLastError();   // start from a clean error state
   if (bf16) {
-    if (causal) fa_fwd_kernel<D, true, true><<<grid, block, 0, stream>>>(a);
+    if (band) fa_fwd_kernel<D, true, true><<<grid, block, 0, stream>>>(a);
     else fa_fwd_kernel<D, true, false><<<grid, block, 0, stream>>>(a);
   } else {
-    if (causal) fa_fwd_kernel<D, false, true><<<grid, block, 0, stream>>>(a);
+    if (band) fa_fwd_kernel<D, false, true><<<grid, block, 0, stream>>>(a);
     else fa_fwd_kernel<D, false, false><<<grid, block, 0, stream>>>(a);
   }
   return hipGetLastError();

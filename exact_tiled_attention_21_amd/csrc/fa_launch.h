@@ -17,6 +17,9 @@ struct FwdArgs {
   int n_qtiles;    // ceil(Nq / rows per workgroup)
   float sl2;       // |scale| * log2(e)
   int negate_q;    // scale < 0: the kernel flips the sign of Q instead
+  // band of visible keys for query i (diag = Nk - Nq): i + diag - wl <= j <= i + diag + wr;
+  // -1 leaves that side open. Causal is wl = -1, wr = 0.
+  int wl, wr;
   // packed variable-length batch (cu_q non-null): q/o are [total_q][Hq][d], k/v
   // [total_k][Hkv][d], lse [Hq][total_q]; sequence b owns rows cu_q[b] ..
   // cu_q[b+1] of q and cu_k[b] .. cu_k[b+1] of k; Nq is the longest query count
@@ -50,7 +53,8 @@ struct DecodeArgs {
 // Rows of queries one forward workgroup covers (32 per wave).
 constexpr int fwd_rows(int) { return 128; }
 
-hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
+// band: apply the (wl, wr) band (causal or a sliding window)
+hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool band, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
 
 }  // namespace fa

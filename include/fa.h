@@ -83,6 +83,21 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  fa_dtype dtype, void* stream);
 
 /*
+ * Attention forward pass with a sliding window (local attention;
+ * "flash-attention-v100" README, How to use FlashAttention: window_size, and
+ * Changelog 2.3): query i sees key j iff
+ *   i + Nk - Nq - window_left <= j <= i + Nk - Nq + window_right,
+ * the band aligned to the bottom-right corner like the causal mask; -1 leaves
+ * a side unbounded. causal = 1 sets window_right to 0. A row that sees no key
+ * gets O = 0 and LSE = -inf. fa_fwd is this call with window (-1, -1).
+ * Other arguments, layouts and status codes as in fa_fwd; FA_ERR_SHAPE for a
+ * window side below -1.
+ */
+fa_status fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Nq, int Nk, int Hq, int Hkv, int d, int window_left,
+                        int window_right, int causal, float scale, fa_dtype dtype, void* stream);
+
+/*
  * Attention forward pass over a packed batch of variable-length sequences (the
  * flash_attn_varlen_func entry point named in the "flash-attention-v100"
  * README, Changelog 2.0; the argument reading is ours): sequence b owns query

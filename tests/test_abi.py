@@ -146,3 +146,9 @@ def fwd_varlen(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cq=FAKE, ck=FAKE, 
 ])
 def test_fwd_varlen_rejects_invalid_arguments(lib, kw, status):
     assert fwd_varlen(lib, **kw) == status
+
+
+@pytest.mark.parametrize("wl,wr,status", [(-2, 0, 2), (0, -2, 2), (-1, -1, 1)])
+def test_fwd_window_rejects_invalid_windows(lib, wl, wr, status):
+    q = None if status == 1 else FAKE   # a valid window reaches the pointer check
+    assert lib.fa_fwd_window(q, FAKE, FAKE, FAKE, FAKE, 1, 8, 8, 2, 1, 64, wl, wr, 0, 0.125, 0, None) == status
