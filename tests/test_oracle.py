@@ -227,6 +227,38 @@ def test_window_zero_zero_selects_the_diagonal_key():
         np.testing.assert_allclose(o[0, i, 0], v[0, i + 3, 0], atol=1e-15)
 
 
+def test_window_open_left_right_zero_equals_causal():
+    # the causal mask is the band with no left limit and right edge 0
+    q, k, v = rand(2, 9, 4, 6), rand(2, 13, 2, 6), rand(2, 13, 2, 6)
+    o1, l1 = oracle.attention(q, k, v, window=(-1, 0))
+    o2, l2 = oracle.attention(q, k, v, causal=True)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_window_wider_than_the_keys_changes_nothing():
+    q, k, v = rand(1, 6, 2, 4), rand(1, 10, 2, 4), rand(1, 10, 2, 4)
+    o1, l1 = oracle.attention(q, k, v, window=(50, 50))
+    o2, l2 = oracle.attention(q, k, v)
+    np.testing.assert_allclose(o1, o2, atol=1e-15)
+    np.testing.assert_allclose(l1, l2, atol=1e-15)
+
+
+@pytest.mark.parametrize("window", [(2, 1), (0, 3), (4, 0), (1, 1)])
+def test_window_row_equals_plain_attention_over_its_key_slice(window):
+    # each row of a band is plain (unmasked) attention over the slice of keys
+    # [i + Nk - Nq - left, i + Nk - Nq + right], cut out in Python
+    Nq, Nk = 6, 11
+    q, k, v = rand(1, Nq, 2, 5), rand(1, Nk, 1, 5), rand(1, Nk, 1, 5)
+    o, lse = oracle.attention(q, k, v, window=window)
+    for i in range(Nq):
+        lo = max(0, i + Nk - Nq - window[0])
+        hi = min(Nk, i + Nk - Nq + window[1] + 1)
+        ob, lb = oracle.attention(q[:, i:i + 1], k[:, lo:hi], v[:, lo:hi])
+        np.testing.assert_allclose(o[:, i:i + 1], ob, atol=1e-14)
+        np.testing.assert_allclose(lse[:, :, i:i + 1], lb, atol=1e-14)
+
+
 def test_seqlens_k_equals_truncated_cache():
     q, k, v = rand(3, 2, 4, 8), rand(3, 20, 2, 8), rand(3, 20, 2, 8)
     lens = np.array([20, 7, 1], np.int32)
