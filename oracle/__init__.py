@@ -7,6 +7,9 @@ binding never do. It shares no code with the HIP kernels.
 Contents
   attention()        fp64 attention by its definition, in C with OpenMP
                      (attention_f64.c), for any shape
+  backward()         fp64 gradients of that definition (dQ, dK, dV for an
+                     upstream dO), written out with numpy matrix products
+  mask_matrix()      the visibility rule of visible() as a boolean matrix
   brute_force()      the same definition as plain Python loops with math.fsum,
                      for tiny shapes; it cross-checks the C routine
   combine_splits()   the third Flash-Decoding step in fp64
@@ -186,3 +189,60 @@ def combine_splits(o_parts, lse_parts):
     wn = np.where(finite[None], w / np.where(finite, tot, 1.0)[None], 0.0)
     o = np.einsum("sbhi,sbihc->bihc", wn, o_parts)
     return o, lse
+
+
+def mask_matrix(Nq, Nk, causal=False, window=(-1, -1)):
+    """Boolean [Nq, Nk]: may query i see key j? The rule of visible(), vectorised."""
+    i = np.arange(Nq)[:, None]
+    j = np.arange(Nk)[None, :]
+    diag = i + Nk - Nq
+    m = np.ones((Nq, Nk), bool)
+    if causal:
+        m &= j <= diag
+    if window[0] >= 0:
+        m &= j >= diag - window[0]
+    if window[1] >= 0:
+        m &= j <= diag + window[1]
+    return m
+
+
+def backward(q, k, v, do, causal=False, scale=None, window=(-1, -1)):
+    """fp64 gradients of L = sum(dO * O) for O = attention(q, k, v): (dq, dk, dv).
+
+    The gradient of the definition, written out (softmax Jacobian):
+      P = softmax(scale Q K^T) over the visible keys (0 elsewhere),
+      dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(P * dP)),
+      dQ = scale dS K, dK = scale dS^T Q;
+    key/value heads shared by a group of query heads collect the gradients of
+    every head of the group. Rows that see no key have P = 0 and contribute
+    nothing."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    group = Hq // Hkv
+    vis = mask_matrix(Nq, Nk, causal, window)
+    has = vis.any(axis=1)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            qh, kh, vh, doh = q[b, :, h], k[b, :, g], v[b, :, g], do[b, :, h]
+            s = scale * (qh @ kh.T)
+            s = np.where(vis, s, -np.inf)
+            m = np.where(has, s.max(axis=1), 0.0)
+            e = np.where(vis, np.exp(s - m[:, None]), 0.0)
+            den = e.sum(axis=1)
+            p = e / np.where(has, den, 1.0)[:, None]
+            dp = doh @ vh.T
+            ds = p * (dp - (p * dp).sum(axis=1)[:, None])
+            dq[b, :, h] = scale * (ds @ kh)
+            dk[b, :, g] += scale * (ds.T @ qh)
+            dv[b, :, g] += p.T @ doh
+    return dq, dk, dv

@@ -309,3 +309,68 @@ def test_flop_convention_matches_pages_table():
     assert w.pairs() == 1024 * 1024
     c = synthetic.WORKLOADS["long_f16_2048_causal"]
     assert c.pairs() == 2048 * 2049 // 2
+
+
+
+# ---------------------------------------------------------------- backward
+
+def test_mask_matrix_equals_visible():
+    for Nq, Nk, causal, window in [(5, 5, True, (-1, -1)), (4, 9, False, (2, 1)), (9, 4, True, (1, -1)),
+                                   (6, 6, False, (0, 0)), (3, 7, False, (-1, 2))]:
+        m = oracle.mask_matrix(Nq, Nk, causal, window)
+        for i in range(Nq):
+            for j in range(Nk):
+                assert m[i, j] == oracle.visible(i, j, Nq, Nk, causal, window)
+
+
+def _loss(q, k, v, do, **kw):
+    o, _ = oracle.attention(q, k, v, **kw)
+    return float(np.sum(do * o))
+
+
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (False, (1, 1))])
+def test_backward_matches_central_differences(causal, window):
+    # the gradient of L = sum(dO * O) by finite differences of the forward oracle,
+    # element by element: independent of the gradient formula
+    B, Nq, Nk, Hq, Hkv, d = 1, 3, 5, 2, 1, 3
+    q, k, v, do = rand(B, Nq, Hq, d), rand(B, Nk, Hkv, d), rand(B, Nk, Hkv, d), rand(B, Nq, Hq, d)
+    dq, dk, dv = oracle.backward(q, k, v, do, causal=causal, window=window)
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            lp = _loss(q, k, v, do, causal=causal, window=window)
+            x[idx] = old - eps
+            lm = _loss(q, k, v, do, causal=causal, window=window)
+            x[idx] = old
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=0, atol=2e-8)
+
+
+def test_backward_matches_torch_autograd_with_gqa():
+    # torch autograd of a plainly written fp64 forward, with K/V heads repeated per group
+    import torch
+    B, Nq, Nk, Hq, Hkv, d = 2, 17, 23, 6, 2, 8
+    q, k, v, do = rand(B, Nq, Hq, d), rand(B, Nk, Hkv, d), rand(B, Nk, Hkv, d), rand(B, Nq, Hq, d)
+    scale = 0.37
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    kk = tk.repeat_interleave(Hq // Hkv, dim=2)
+    vv = tv.repeat_interleave(Hq // Hkv, dim=2)
+    s = torch.einsum("bihc,bjhc->bhij", tq, kk) * scale
+    mask = torch.ones(Nq, Nk, dtype=torch.bool).tril(diagonal=Nk - Nq)
+    s = s.masked_fill(~mask, float("-inf"))
+    o = torch.einsum("bhij,bjhc->bihc", torch.softmax(s, dim=-1), vv)
+    (o * torch.tensor(do)).sum().backward()
+    dq, dk, dv = oracle.backward(q, k, v, do, causal=True, scale=scale)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+
+
+def test_backward_rows_without_keys_have_zero_gradient():
+    q, k, v, do = rand(1, 6, 2, 4), rand(1, 3, 2, 4), rand(1, 3, 2, 4), rand(1, 6, 2, 4)
+    dq, dk, dv = oracle.backward(q, k, v, do, causal=True)
+    # causal with Nq = 6 > Nk = 3: rows 0..2 see no key
+    assert np.all(dq[0, :3] == 0) and np.all(np.isfinite(dk)) and np.all(np.isfinite(dv))
