@@ -9,6 +9,8 @@ kernels of libfa.so. torch supplies device memory and the current stream.
   decode(q, k_cache, v_cache, num_splits=16, scale=None, causal=False) -> (o, lse)
   decode_paged(q, k_pages, v_pages, block_table, cache_seqlens, num_splits=16,
                scale=None, causal=False) -> (o, lse)
+  attention_backward(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
+  attention_func(q, k, v, causal=False, scale=None) -> o, differentiable
 
 Tensors are [batch, seq_len, heads, head_dim], fp16 or bf16, contiguous, on a
 ROCm device; lse is float32 [batch, heads, seq_len_q]. The default scale is
@@ -21,7 +23,8 @@ import math
 
 from ._lib import FA_BF16, FA_F16, FA_MAX_SPLITS, FaError, load, status_str  # noqa: F401
 
-__all__ = ["attention", "attention_varlen", "decode", "decode_paged", "decode_workspace_bytes", "FaError", "load"]
+__all__ = ["attention", "attention_varlen", "attention_backward", "attention_func", "bwd_workspace_bytes", "decode",
+           "decode_paged", "decode_workspace_bytes", "FaError", "load"]
 
 
 def _torch():
@@ -192,3 +195,73 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, cau
     if st != 0:
         raise FaError(st, "fa_fwd_varlen")
     return o, lse_t
+
+
+def bwd_workspace_bytes(B: int, Nq: int, Hq: int) -> int:
+    return int(load().fa_bwd_workspace_bytes(B, Nq, Hq))
+
+
+def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+                       workspace=None, dq=None, dk=None, dv=None):
+    """Gradients (dq, dk, dv) of attention(q, k, v, causal, scale) for the upstream
+    gradient dout, from the forward's output o and lse (float32 [B, Hq, Nq])."""
+    torch = _torch()
+    _check(q, k, v)
+    for name, t in (("o", o), ("dout", dout)):
+        if not t.is_cuda or t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor shaped and typed like q")
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if (not lse.is_cuda or lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq)
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 device tensor [B, Hq, Nq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = bwd_workspace_bytes(B, Nq, Hq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    with torch.cuda.device(q.device):
+        st = load().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Nq, Nk, Hq, Hkv, d,
+                           int(bool(causal)), float(scale), _dtype_code(q), workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def _autograd_function():
+    torch = _torch()
+
+    class _Attention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, causal, scale):
+            o, lse = attention(q, k, v, causal=causal, scale=scale)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.causal, ctx.scale = causal, scale
+            return o
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, o, lse = ctx.saved_tensors
+            dq, dk, dv = attention_backward(q, k, v, o, lse, dout.contiguous(), causal=ctx.causal,
+                                            scale=ctx.scale)
+            return dq, dk, dv, None, None
+
+    return _Attention
+
+
+_ATTN_FN = None
+
+
+def attention_func(q, k, v, causal: bool = False, scale: float | None = None):
+    """attention(...)[0] as a differentiable torch op (forward and backward in libfa)."""
+    global _ATTN_FN
+    if _ATTN_FN is None:
+        _ATTN_FN = _autograd_function()
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    return _ATTN_FN.apply(q, k, v, bool(causal), float(scale))

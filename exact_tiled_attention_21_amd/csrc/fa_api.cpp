@@ -19,6 +19,12 @@ hipError_t launch_decode_d96(const DecodeArgs&, bool, bool, hipStream_t);
 hipError_t launch_decode_d128(const DecodeArgs&, bool, bool, hipStream_t);
 hipError_t launch_decode_d192(const DecodeArgs&, bool, bool, hipStream_t);
 hipError_t launch_decode_d256(const DecodeArgs&, bool, bool, hipStream_t);
+hipError_t launch_bwd_d32(const BwdArgs&, bool, bool, hipStream_t);
+hipError_t launch_bwd_d64(const BwdArgs&, bool, bool, hipStream_t);
+hipError_t launch_bwd_d96(const BwdArgs&, bool, bool, hipStream_t);
+hipError_t launch_bwd_d128(const BwdArgs&, bool, bool, hipStream_t);
+hipError_t launch_bwd_d192(const BwdArgs&, bool, bool, hipStream_t);
+hipError_t launch_bwd_d256(const BwdArgs&, bool, bool, hipStream_t);
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool band, hipStream_t s) {
   switch (d) {
@@ -40,6 +46,18 @@ hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, bool causal, hip
     case 128: return launch_decode_d128(a, bf16, causal, s);
     case 192: return launch_decode_d192(a, bf16, causal, s);
     case 256: return launch_decode_d256(a, bf16, causal, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool causal, hipStream_t s) {
+  switch (d) {
+    case 32: return launch_bwd_d32(a, bf16, causal, s);
+    case 64: return launch_bwd_d64(a, bf16, causal, s);
+    case 96: return launch_bwd_d96(a, bf16, causal, s);
+    case 128: return launch_bwd_d128(a, bf16, causal, s);
+    case 192: return launch_bwd_d192(a, bf16, causal, s);
+    case 256: return launch_bwd_d256(a, bf16, causal, s);
   }
   return hipErrorInvalidValue;
 }
@@ -220,6 +238,39 @@ fa_status fa_decode_splitkv_paged(const void* q, const void* k_pages, const void
                               workspace, stream);
 }
 
+size_t fa_bwd_workspace_bytes(int B, int Nq, int Hq) {
+  if (B < 1 || Nq < 1 || Hq < 1) return 0;
+  const size_t rows = size_t(B) * Hq * ((size_t(Nq) + 31) / 32 * 32);
+  return 2 * pad256(rows * sizeof(float));
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, int B, int Nq, int Nk, int Hq,
+                 int Hkv, int d, int causal, float scale, fa_dtype dtype, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  fa_status st = check_common(q, k, v, const_cast<void*>(o), lse, B, Nq, Nk, Hq, Hkv, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_NULLPTR;
+  if (workspace_bytes < fa_bwd_workspace_bytes(B, Nq, Hq)) return FA_ERR_WORKSPACE;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return FA_ERR_ALIGN;
+  const int64_t nkt = (int64_t(Nk) + 127) / 128, nqt = (int64_t(Nq) + 127) / 128;
+  if (nkt * Hkv * B > 0x7fffffffLL || nqt * Hq * B > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (int64_t(B) * Hq * ((int64_t(Nq) + 31) / 32 * 32) > 0x3fffffffLL) return FA_ERR_SHAPE;
+  fa::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  const size_t rows = size_t(B) * Hq * ((size_t(Nq) + 31) / 32 * 32);
+  a.dsum = static_cast<float*>(workspace);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + pad256(rows * sizeof(float)));
+  a.B = B; a.Nq = Nq; a.Nk = Nk; a.Hq = Hq; a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  a.sl2 = scale * 1.4426950408889634f;
+  a.scale = scale;
+  hipError_t e = fa::launch_bwd(a, d, dtype == FA_BF16, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 const char* fa_status_str(fa_status s) {
   switch (s) {
     case FA_OK: return "ok";
@@ -229,7 +280,7 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_HEADDIM: return "head dim must be one of 32, 64, 96, 128, 192, 256";
     case FA_ERR_DTYPE: return "dtype must be FA_F16 or FA_BF16";
     case FA_ERR_SPLITS: return "num_splits must be in 1..FA_MAX_SPLITS";
-    case FA_ERR_WORKSPACE: return "workspace smaller than fa_decode_workspace_bytes()";
+    case FA_ERR_WORKSPACE: return "workspace smaller than the size its *_workspace_bytes() call gives";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA_ERR_SCALE: return "scale is not finite";

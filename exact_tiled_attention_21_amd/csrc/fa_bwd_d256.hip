@@ -1,0 +1,8 @@
+// Backward-pass instances for head dim 256.
+#include "fa_bwd_kernel.h"
+
+namespace fa {
+hipError_t launch_bwd_d256(const BwdArgs& a, bool bf16, bool causal, hipStream_t stream) {
+  return launch_bwd_d<256>(a, bf16, causal, stream);
+}
+}  // namespace fa

@@ -1,0 +1,511 @@
+// Exact attention backward pass on gfx950 (MFMA 32x32x16).
+//
+// For O = softmax(scale Q K^T) V (with the causal mask, if any) and an upstream
+// gradient dO, with P the softmax probabilities and D_i = sum_c dO[i][c] O[i][c]:
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+// As in the forward pass no score matrix is stored: P is recomputed tile by tile
+// from the forward's log-sum-exp as exp(scale s - LSE) ("flash-attention-v100"
+// README: forward and backward passes for head dims up to 256, and a
+// deterministic backward option). This is the deterministic form, with no
+// atomics, in three kernels:
+//   fa_bwd_pre_kernel   D per query row, and the LSE in log2 units (+inf for a
+//                       row with no visible key and for the padding rows, so
+//                       their P is exactly 0), stored [B][Hq][Nq rounded to 32];
+//   fa_bwd_dkdv_kernel  one workgroup per 128 keys of a KV head, walking every
+//                       query head of its group and every query tile; owns dK
+//                       and dV of its keys. Orientation S = Q K^T: a lane owns a
+//                       key, so P and dS leave the accumulators as the B
+//                       operands of dV^T += dO^T P and dK^T += Q^T dS;
+//   fa_bwd_dq_kernel    one workgroup per 128 query rows of a head, walking the
+//                       key tiles; owns dQ of its rows. Orientation S^T = K Q^T
+//                       as in the forward: dS^T feeds the B operand of
+//                       dQ^T += K^T dS^T.
+// The two passes recompute S and dP, seven tile products per (query, key) tile
+// pair against five with a shared pass, and in exchange need no fp32 atomics
+// and give bit-identical results from run to run.
+#pragma once
+
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+template <int D> struct BwdCfg {
+  static constexpr int NW = 4;                      // waves per workgroup
+  static constexpr int THREADS = NW * 64;
+  static constexpr int BT = 32;                     // rows of one tile (queries or keys)
+  static constexpr int WROWS = NW * BT;             // rows a workgroup owns
+  static constexpr int NS = D / 16;                 // 16-wide d slices
+  static constexpr int NCB = D / 32;                // 32-wide d blocks
+  static constexpr int TILE = BT * D * 2;           // bytes of one [32][D] tile
+  static constexpr int NPIECE = TILE / 1024;        // 1 KB DMA pieces per tile
+  static constexpr int NDMA = (NPIECE + NW - 1) / NW;
+  static constexpr bool EVEN = NPIECE % NW == 0;
+  static_assert(TILE % 1024 == 0, "tile must split into whole DMA pieces");
+};
+
+// DMA of [32][D] row tiles (row pitch `pitch` bytes) into swizzled LDS. Piece
+// i of this wave fills LDS bytes [(i NW + wave) 1024, +1024): lane l writes the
+// 16 bytes at +16 l, physical chunk pch of row r, so it fetches logical chunk
+// pch ^ swz(r) of that row. Bytes at or past `valid` read as zero.
+template <int D> struct BwdDma {
+  using C = BwdCfg<D>;
+  uint32_t goff[C::NDMA];
+  int wave;
+  __device__ __forceinline__ void init(uint32_t pitch, int wave_, int lane) {
+    wave = wave_;
+#pragma unroll
+    for (int i = 0; i < C::NDMA; ++i) {
+      const uint32_t p = (i * C::NW + wave) * 1024 + lane * 16;
+      const uint32_t r = p / (D * 2), pch = (p % (D * 2)) / 16;
+      goff[i] = r * pitch + ((pch ^ Swz<D>::f(r)) << 4);
+    }
+  }
+  __device__ __forceinline__ void issue(const char* base, int64_t valid, char* lds) const {
+    const uint32_t nrec = valid > 0 ? static_cast<uint32_t>(valid > 0x7fffffff ? 0x7fffffff : valid) : 0u;
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, nrec, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < C::NDMA; ++i)
+      if (C::EVEN || i * C::NW + wave < C::NPIECE)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(lds + (i * C::NW + wave) * 1024), 16, goff[i], 0, 0, 0);
+  }
+};
+
+// Two LDS stages of two [32][D] tiles each (Q and dO, or K and V).
+struct BwdLds {
+  char* x[2];
+  char* y[2];
+};
+
+// A-operand fragment of the rows of a swizzled [32][D] tile: 32 rows x d slice s.
+template <int D, typename V8>
+__device__ __forceinline__ V8 row_frag(const char* t, int s, int lane) {
+  return lds_read_v8<V8>(t, Swz<D>::off(lane & 31, 2u * s + (lane >> 5)));
+}
+
+// Padded row count of the per-row statistics.
+__host__ __device__ constexpr int bwd_nq_pad(int nq) { return (nq + 31) / 32 * 32; }
+
+// ---------------------------------------------------------------- preprocess
+
+// G lanes per statistics entry (b, h, i), i < Nq rounded up to 32:
+// D = sum_c dO * O in fp32 and the LSE in log2 units; padding rows and rows
+// that saw no key get D = 0, LSE = +inf.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const BwdArgs a) {
+  using T = typename Elem<BF16>::T;
+  typedef T T8 __attribute__((ext_vector_type(8)));
+  constexpr int CPR = D / 8;                              // 16-byte chunks per row
+  constexpr int G = CPR <= 4 ? 4 : CPR <= 8 ? 8 : CPR <= 16 ? 16 : 32;
+  constexpr int RPB = 256 / G;
+  const int nqp = bwd_nq_pad(a.Nq);
+  const int64_t entries = static_cast<int64_t>(a.B) * a.Hq * nqp;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / G;
+  const int c = threadIdx.x % G;
+  const int i = static_cast<int>(e % nqp);
+  const int64_t bh = e / nqp;
+  const int h = static_cast<int>(bh % a.Hq);
+  const int64_t b = bh / a.Hq;
+  const bool live = e < entries && i < a.Nq;
+  float acc = 0.f;
+  if (live && c < CPR) {
+    const int64_t row = ((b * a.Nq + i) * a.Hq + h) * D + 8 * c;
+    const T8 o8 = *reinterpret_cast<const T8*>(reinterpret_cast<const T*>(a.o) + row);
+    const T8 d8 = *reinterpret_cast<const T8*>(reinterpret_cast<const T*>(a.dout) + row);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc = __builtin_fmaf(static_cast<float>(o8[k]), static_cast<float>(d8[k]), acc);
+  }
+#pragma unroll
+  for (int m = G / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, G);
+  if (e < entries && c == 0) {
+    float l2 = __builtin_huge_valf();
+    if (live) {
+      const float l = a.lse[bh * a.Nq + i];
+      if (l != kNegInf) l2 = l * kLog2e;
+    }
+    a.dsum[e] = live ? acc : 0.f;
+    a.lse2[e] = l2;
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+
+template <int D, bool BF16, bool CAUSAL> struct DkdvWave {
+  using C = BwdCfg<D>;
+  using E = Elem<BF16>;
+  using T = typename E::T;
+  using V8 = typename E::V8;
+
+  const BwdArgs& a;
+  int lane, wave, hh;
+  int b, g, key, k0w, diag;
+  int nqt, t0, nqp;
+  uint32_t qpitch;
+  V8 kf[C::NS], vf[C::NS];          // this lane's key row of K and V (B operands)
+  f32x16 dvt[C::NCB], dkt[C::NCB];  // dV^T and dK^T, [d][key]
+  // log2 LSE and D of the 16 query rows of this lane's accumulator registers,
+  // per stage (loaded one step ahead, with the tiles)
+  f32x4 sl[2][4], sd[2][4];
+  BwdDma<D> dma;
+
+  __device__ __forceinline__ DkdvWave(const BwdArgs& args, int b_, int g_, int k0) : a(args), b(b_), g(g_) {
+    lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    hh = lane >> 5;
+    k0w = k0 + wave * C::BT;
+    key = k0w + (lane & 31);
+    diag = a.Nk - a.Nq;
+    nqt = (a.Nq + C::BT - 1) / C::BT;
+    nqp = bwd_nq_pad(a.Nq);
+    // causal: query tiles before the first row that sees key k0 contribute nothing
+    t0 = CAUSAL ? min(nqt, max(0, k0 - diag) / C::BT) : 0;
+    qpitch = static_cast<uint32_t>(a.Hq) * D * 2;
+    const size_t kv = ((static_cast<size_t>(b) * a.Nk + key) * a.Hkv + g) * D + 8 * hh;
+    const T* kp = reinterpret_cast<const T*>(a.k) + kv;
+    const T* vp = reinterpret_cast<const T*>(a.v) + kv;
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) {
+      kf[s] = key < a.Nk ? *reinterpret_cast<const V8*>(kp + 16 * s) : V8{};
+      vf[s] = key < a.Nk ? *reinterpret_cast<const V8*>(vp + 16 * s) : V8{};
+    }
+#pragma unroll
+    for (int cb = 0; cb < C::NCB; ++cb) {
+      dvt[cb] = f32x16{};
+      dkt[cb] = f32x16{};
+    }
+    dma.init(qpitch, wave, lane);
+  }
+
+  // Q and dO rows t*32 .. of query head hi of the group into one stage, and
+  // the statistics of those rows (rows 8 gq + 4 hh + 0..3 into sl/sd[gq])
+  __device__ __forceinline__ void fetch(int hi, int t, char* ql, char* ol, f32x4 (&l)[4], f32x4 (&dd)[4]) const {
+    const size_t si = (static_cast<size_t>(b) * a.Hq + g * a.group + hi) * nqp + t * C::BT + 4 * hh;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      l[gq] = *reinterpret_cast<const f32x4*>(a.lse2 + si + 8 * gq);
+      dd[gq] = *reinterpret_cast<const f32x4*>(a.dsum + si + 8 * gq);
+    }
+    const size_t off = ((static_cast<size_t>(b) * a.Nq + t * C::BT) * a.Hq + g * a.group + hi) * D * 2;
+    const int64_t valid = static_cast<int64_t>(a.Nq - t * C::BT - 1) * qpitch + D * 2;
+    dma.issue(reinterpret_cast<const char*>(a.q) + off, valid, ql);
+    dma.issue(reinterpret_cast<const char*>(a.dout) + off, valid, ol);
+  }
+
+  // Tile t of query head hi (stage ST): S = Q K^T and dP = dO V^T with the query
+  // rows in registers (row q0 + 8 (r / 4) + 4 hh + r % 4 in register r), then
+  // dV^T += dO^T P and dK^T += Q^T dS over those rows. The transposed tiles
+  // come from v_frag, whose row order matches the one the accumulator gives P
+  // and dS as B operands. The next tile (in head-major order) is fetched first.
+  template <int ST, bool MASK>
+  __device__ __forceinline__ void step(int hi, int t, const BwdLds& lds) {
+    {
+      int hn = hi, tn = t + 1;
+      if (tn == nqt) {
+        hn = hi + 1;
+        tn = t0;
+      }
+      if (hn < a.group) fetch(hn, tn, lds.x[ST ^ 1], lds.y[ST ^ 1], sl[ST ^ 1], sd[ST ^ 1]);
+    }
+    const char* qt = lds.x[ST];
+    const char* ot = lds.y[ST];
+    const int q0 = t * C::BT;
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int i = 0; i < C::NS; ++i) {
+      s = E::mfma(row_frag<D, V8>(qt, i, lane), kf[i], s);
+      dp = E::mfma(row_frag<D, V8>(ot, i, lane), vf[i], dp);
+    }
+    f32x16 p, ds;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float pr = exp2_fast(__builtin_fmaf(s[r], a.sl2, -sl[ST][r >> 2][r & 3]));
+      if (MASK) {
+        const int q = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        pr = (key > q + diag) ? 0.f : pr;
+      }
+      p[r] = pr;
+      ds[r] = pr * (dp[r] - sd[ST][r >> 2][r & 3]);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const V8 pf = to_v8<BF16>(p, 8 * u);
+      const V8 dsf = to_v8<BF16>(ds, 8 * u);
+#pragma unroll
+      for (int cb = 0; cb < C::NCB; ++cb) {
+        dvt[cb] = E::mfma(v_frag<D, V8>(ot, cb, u, lane), pf, dvt[cb]);
+        dkt[cb] = E::mfma(v_frag<D, V8>(qt, cb, u, lane), dsf, dkt[cb]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // tiles [t, te) of head hi; n counts the steps taken (stage = n & 1)
+  template <bool MASK>
+  __device__ __forceinline__ void run(int hi, int t, int te, int& n, const BwdLds& lds) {
+    if (t < te && (n & 1)) {
+      step<1, MASK>(hi, t, lds);
+      ++t;
+      ++n;
+    }
+    for (; t + 2 <= te; t += 2, n += 2) {
+      step<0, MASK>(hi, t, lds);
+      step<1, MASK>(hi, t + 1, lds);
+    }
+    if (t < te) {
+      step<0, MASK>(hi, t, lds);
+      ++n;
+    }
+  }
+
+  // dV, and dK = scale (dK^T)^T, rounded to the element type
+  __device__ __forceinline__ void finish() const {
+    if (key >= a.Nk) return;
+    const size_t row = ((static_cast<size_t>(b) * a.Nk + key) * a.Hkv + g) * D;
+    T* dvp = reinterpret_cast<T*>(a.dv) + row;
+    T* dkp = reinterpret_cast<T*>(a.dk) + row;
+    typedef T T4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int cb = 0; cb < C::NCB; ++cb)
+#pragma unroll
+      for (int gr = 0; gr < 4; ++gr) {
+        T4 wv, wk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wv[e] = static_cast<T>(dvt[cb][4 * gr + e]);
+          wk[e] = static_cast<T>(dkt[cb][4 * gr + e] * a.scale);
+        }
+        *reinterpret_cast<T4*>(dvp + 32 * cb + 8 * gr + 4 * hh) = wv;
+        *reinterpret_cast<T4*>(dkp + 32 * cb + 8 * gr + 4 * hh) = wk;
+      }
+  }
+};
+
+template <int D, bool BF16, bool CAUSAL>
+__global__ __launch_bounds__(BwdCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dkdv_kernel(const BwdArgs a) {
+  using C = BwdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char q_lds0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char q_lds1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char o_lds0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char o_lds1[C::TILE];
+
+  const int nkt = (a.Nk + C::WROWS - 1) / C::WROWS;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int kt = bid % nkt;
+  const int gb = bid / nkt;
+  const int g = gb % a.Hkv;
+  const int b = gb / a.Hkv;
+  const int k0 = kt * C::WROWS;
+  DkdvWave<D, BF16, CAUSAL> w(a, b, g, k0);
+  const BwdLds lds{{q_lds0, q_lds1}, {o_lds0, o_lds1}};
+
+  // causal: tiles [t0, tm) hold rows for which some key of the workgroup is
+  // masked (the diagonal); later tiles see every key of it
+  int tm = w.t0;
+  if (CAUSAL) {
+    const int x = k0 + C::WROWS - w.diag;   // first row that sees every key
+    tm = min(w.nqt, max(w.t0, x > 0 ? (x + C::BT - 1) / C::BT : 0));
+  }
+  if (w.t0 < w.nqt) w.fetch(0, w.t0, lds.x[0], lds.y[0], w.sl[0], w.sd[0]);
+  __syncthreads();
+  int n = 0;
+  for (int hi = 0; hi < a.group && w.t0 < w.nqt; ++hi) {
+    w.template run<true>(hi, w.t0, tm, n, lds);
+    w.template run<false>(hi, tm, w.nqt, n, lds);
+  }
+  w.finish();
+}
+
+// ---------------------------------------------------------------- dQ
+
+template <int D, bool BF16, bool CAUSAL> struct DqWave {
+  using C = BwdCfg<D>;
+  using E = Elem<BF16>;
+  using T = typename E::T;
+  using V8 = typename E::V8;
+
+  const BwdArgs& a;
+  int lane, wave, hh;
+  int b, hq, qrow, diag;
+  float lse2, dsum;
+  const char* kg;
+  const char* vg;
+  int64_t valid;
+  uint32_t kpitch;
+  int nsteps;
+  V8 qf[C::NS], of[C::NS];   // this lane's query row of Q and dO (B operands)
+  f32x16 dqt[C::NCB];        // dQ^T, [d][q]
+  BwdDma<D> dma;
+
+  __device__ __forceinline__ DqWave(const BwdArgs& args, int b_, int hq_, int q0) : a(args), b(b_), hq(hq_) {
+    lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    hh = lane >> 5;
+    qrow = q0 + wave * C::BT + (lane & 31);
+    diag = a.Nk - a.Nq;
+    nsteps = 0;
+    const bool live = qrow < a.Nq;
+    const size_t r = ((static_cast<size_t>(b) * a.Nq + qrow) * a.Hq + hq) * D + 8 * hh;
+    const T* qp = reinterpret_cast<const T*>(a.q) + r;
+    const T* op = reinterpret_cast<const T*>(a.dout) + r;
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) {
+      qf[s] = live ? *reinterpret_cast<const V8*>(qp + 16 * s) : V8{};
+      of[s] = live ? *reinterpret_cast<const V8*>(op + 16 * s) : V8{};
+    }
+    const size_t si = (static_cast<size_t>(b) * a.Hq + hq) * bwd_nq_pad(a.Nq) + qrow;
+    lse2 = live ? a.lse2[si] : __builtin_huge_valf();
+    dsum = live ? a.dsum[si] : 0.f;
+#pragma unroll
+    for (int cb = 0; cb < C::NCB; ++cb) dqt[cb] = f32x16{};
+    kpitch = static_cast<uint32_t>(a.Hkv) * D * 2;
+    const size_t head = ((static_cast<size_t>(b) * a.Nk) * a.Hkv + hq / a.group) * D * 2;
+    kg = reinterpret_cast<const char*>(a.k) + head;
+    vg = reinterpret_cast<const char*>(a.v) + head;
+    valid = static_cast<int64_t>(a.Nk - 1) * kpitch + D * 2;
+    dma.init(kpitch, wave, lane);
+  }
+
+  __device__ __forceinline__ void fetch(int j, char* kl, char* vl) const {
+    const int64_t off = static_cast<int64_t>(j) * C::BT * kpitch;
+    dma.issue(kg + off, valid - off, kl);
+    dma.issue(vg + off, valid - off, vl);
+  }
+
+  // Key tile j (stage ST): S^T = K Q^T and dP^T = V dO^T with the keys in
+  // registers (key 32 j + 8 (r / 4) + 4 hh + r % 4 in register r), then
+  // dQ^T += K^T dS^T. The next key tile is fetched first.
+  template <int ST, bool MASK>
+  __device__ __forceinline__ void step(int j, const BwdLds& lds) {
+    if (j + 1 < nsteps) fetch(j + 1, lds.x[ST ^ 1], lds.y[ST ^ 1]);
+    const char* kt = lds.x[ST];
+    const char* vt = lds.y[ST];
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int i = 0; i < C::NS; ++i) {
+      s = E::mfma(row_frag<D, V8>(kt, i, lane), qf[i], s);
+      dp = E::mfma(row_frag<D, V8>(vt, i, lane), of[i], dp);
+    }
+    f32x16 ds;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float pr = exp2_fast(__builtin_fmaf(s[r], a.sl2, -lse2));
+      if (MASK) {
+        const int kk = j * C::BT + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const bool hide = CAUSAL ? (kk >= a.Nk || kk > qrow + diag) : (kk >= a.Nk);
+        pr = hide ? 0.f : pr;
+      }
+      ds[r] = pr * (dp[r] - dsum);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const V8 dsf = to_v8<BF16>(ds, 8 * u);
+#pragma unroll
+      for (int cb = 0; cb < C::NCB; ++cb) dqt[cb] = E::mfma(v_frag<D, V8>(kt, cb, u, lane), dsf, dqt[cb]);
+    }
+    __syncthreads();
+  }
+
+  // key tiles [j, je), tile j in stage j & 1
+  template <bool MASK>
+  __device__ __forceinline__ void run(int j, int je, const BwdLds& lds) {
+    if (j < je && (j & 1)) {
+      step<1, MASK>(j, lds);
+      ++j;
+    }
+    for (; j + 2 <= je; j += 2) {
+      step<0, MASK>(j, lds);
+      step<1, MASK>(j + 1, lds);
+    }
+    if (j < je) step<0, MASK>(j, lds);
+  }
+
+  __device__ __forceinline__ void finish() const {
+    if (qrow >= a.Nq) return;
+    T* dqp = reinterpret_cast<T*>(a.dq) + ((static_cast<size_t>(b) * a.Nq + qrow) * a.Hq + hq) * D;
+    typedef T T4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int cb = 0; cb < C::NCB; ++cb)
+#pragma unroll
+      for (int gr = 0; gr < 4; ++gr) {
+        T4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = static_cast<T>(dqt[cb][4 * gr + e] * a.scale);
+        *reinterpret_cast<T4*>(dqp + 32 * cb + 8 * gr + 4 * hh) = w;
+      }
+  }
+};
+
+template <int D, bool BF16, bool CAUSAL>
+__global__ __launch_bounds__(BwdCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dq_kernel(const BwdArgs a) {
+  using C = BwdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char k_lds0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[C::TILE];
+
+  const int nqt = (a.Nq + C::WROWS - 1) / C::WROWS;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  int qt = bid % nqt;
+  const int hb = bid / nqt;
+  const int hq = hb % a.Hq;
+  const int b = hb / a.Hq;
+  if (CAUSAL) qt = nqt - 1 - qt;   // longest rows first
+  const int q0 = qt * C::WROWS;
+  DqWave<D, BF16, CAUSAL> w(a, b, hq, q0);
+  const BwdLds lds{{k_lds0, k_lds1}, {v_lds0, v_lds1}};
+
+  // key tiles the workgroup needs (causal: up to its last row's diagonal), and
+  // the first one where some row needs an element mask (key tail, diagonal)
+  const int last = min(q0 + C::WROWS, a.Nq) - 1;
+  const int kend = CAUSAL ? min(a.Nk, last + w.diag + 1) : a.Nk;
+  w.nsteps = kend > 0 ? (kend + C::BT - 1) / C::BT : 0;
+  int jm = a.Nk / C::BT;
+  if (CAUSAL) jm = min(jm, max(0, q0 + w.diag + 1) / C::BT);
+  jm = min(jm, w.nsteps);
+
+  if (w.nsteps > 0) w.fetch(0, lds.x[0], lds.y[0]);
+  __syncthreads();
+  w.template run<false>(0, jm, lds);
+  w.template run<true>(jm, w.nsteps, lds);
+  w.finish();
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs& a, bool bf16, bool causal, hipStream_t stream) {
+  using C = BwdCfg<D>;
+  (void)hipGetLastError();   // start from a clean error state
+  {
+    constexpr int CPR = D / 8;
+    constexpr int G = CPR <= 4 ? 4 : CPR <= 8 ? 8 : CPR <= 16 ? 16 : 32;
+    const int64_t entries = static_cast<int64_t>(a.B) * a.Hq * bwd_nq_pad(a.Nq);
+    const dim3 grid(static_cast<unsigned>((entries + 256 / G - 1) / (256 / G)));
+    if (bf16) fa_bwd_pre_kernel<D, true><<<grid, 256, 0, stream>>>(a);
+    else fa_bwd_pre_kernel<D, false><<<grid, 256, 0, stream>>>(a);
+  }
+  const dim3 block(C::THREADS);
+  const dim3 grid_kv(static_cast<unsigned>((a.Nk + C::WROWS - 1) / C::WROWS) * a.Hkv * a.B);
+  const dim3 grid_q(static_cast<unsigned>((a.Nq + C::WROWS - 1) / C::WROWS) * a.Hq * a.B);
+  if (bf16) {
+    if (causal) {
+      fa_bwd_dkdv_kernel<D, true, true><<<grid_kv, block, 0, stream>>>(a);
+      fa_bwd_dq_kernel<D, true, true><<<grid_q, block, 0, stream>>>(a);
+    } else {
+      fa_bwd_dkdv_kernel<D, true, false><<<grid_kv, block, 0, stream>>>(a);
+      fa_bwd_dq_kernel<D, true, false><<<grid_q, block, 0, stream>>>(a);
+    }
+  } else {
+    if (causal) {
+      fa_bwd_dkdv_kernel<D, false, true><<<grid_kv, block, 0, stream>>>(a);
+      fa_bwd_dq_kernel<D, false, true><<<grid_q, block, 0, stream>>>(a);
+    } else {
+      fa_bwd_dkdv_kernel<D, false, false><<<grid_kv, block, 0, stream>>>(a);
+      fa_bwd_dq_kernel<D, false, false><<<grid_q, block, 0, stream>>>(a);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fa

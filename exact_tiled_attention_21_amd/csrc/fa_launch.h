@@ -50,11 +50,30 @@ struct DecodeArgs {
   int page_size, max_pages, num_pages;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;  // [B][Hq][Nq], natural log, from the forward pass
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;       // workspace [B][Hq][Nq rounded up to 32]: sum_c dO * O
+  float* lse2;       // workspace, same shape: LSE * log2(e), +inf for no key / padding
+  int B, Nq, Nk, Hq, Hkv;
+  int group;         // Hq / Hkv
+  float sl2;         // scale * log2(e)
+  float scale;
+};
+
 // Rows of queries one forward workgroup covers (32 per wave).
 constexpr int fwd_rows(int) { return 128; }
 
 // band: apply the (wl, wr) band (causal or a sliding window)
 hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool band, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
 
 }  // namespace fa

@@ -1,13 +1,17 @@
 /*
  * fa.h -- C ABI of libfa: exact tiled attention on MI355X (gfx950).
  *
- * Two operations:
+ * Three operations:
  *   fa_fwd             the exact attention forward pass, computed tile by tile
  *                      with an online softmax so the Nq x Nk score matrix never
- *                      reaches device memory;
+ *                      reaches device memory (variants: fa_fwd_window,
+ *                      fa_fwd_varlen);
  *   fa_decode_splitkv  the same result for short query blocks, with the keys
  *                      split into chunks that are processed in parallel and a
- *                      second kernel that merges the per-chunk results.
+ *                      second kernel that merges the per-chunk results
+ *                      (variant: fa_decode_splitkv_paged);
+ *   fa_bwd             the gradients dQ, dK, dV of the forward pass, again
+ *                      without storing the score matrix.
  *
  * Definition ("flash-attention-v100" README, How to use FlashAttention):
  *   O = softmax(scale * Q K^T) V, row by row, with
@@ -48,13 +52,13 @@ extern "C" {
 
 typedef enum {
   FA_OK = 0,
-  FA_ERR_NULLPTR = 1,   /* q, k, v or o is NULL (or workspace for decode)   */
+  FA_ERR_NULLPTR = 1,   /* a required pointer is NULL                       */
   FA_ERR_SHAPE = 2,     /* B, Nq, Nk, Hq or Hkv < 1, or a size overflows    */
   FA_ERR_HEADS = 3,     /* Hq is not a multiple of Hkv                      */
   FA_ERR_HEADDIM = 4,   /* d not in {32, 64, 96, 128, 192, 256}             */
   FA_ERR_DTYPE = 5,     /* dtype not FA_F16 or FA_BF16                      */
   FA_ERR_SPLITS = 6,    /* num_splits < 1 or > FA_MAX_SPLITS                */
-  FA_ERR_WORKSPACE = 7, /* workspace_bytes < fa_decode_workspace_bytes(...) */
+  FA_ERR_WORKSPACE = 7, /* workspace_bytes below the *_workspace_bytes size  */
   FA_ERR_LAUNCH = 8,    /* the HIP runtime rejected a kernel launch         */
   FA_ERR_ALIGN = 9,     /* a tensor pointer is not 16-byte aligned          */
   FA_ERR_SCALE = 10     /* scale is not a finite number                     */
@@ -188,6 +192,42 @@ fa_status fa_decode_splitkv_paged(const void* q, const void* k_pages, const void
                                   int page_size, int max_pages_per_seq, int num_splits, int causal,
                                   float scale, fa_dtype dtype, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs: two float32 arrays [B][Hq][Nq'] with
+ * Nq' = Nq rounded up to a multiple of 32, each padded to 256 bytes. Returns 0
+ * for invalid sizes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Nq, int Hq);
+
+/*
+ * Attention backward pass ("flash-attention-v100" README: the package's
+ * backward pass and its deterministic option; Changelog 2.1 for the
+ * bottom-right causal mask it shares with the forward). With P the softmax
+ * probabilities of the forward pass and D_i = sum_c dO[i][c] O[i][c]:
+ *   dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q,
+ * where for grouped-query heads dK and dV of a KV head sum over the query
+ * heads that read it. P is recomputed from `lse`, never stored.
+ *   q, k, v, o : the forward pass's inputs and output (layouts above).
+ *   lse        : float32 [B][Hq][Nq], the forward pass's log-sum-exp
+ *                (required; -inf marks a row with no visible key).
+ *   dout       : dO, [B][Nq][Hq][d] `dtype`.
+ *   dq         : [B][Nq][Hq][d]; dk, dv: [B][Nk][Hkv][d]; all `dtype`, fully
+ *                overwritten, not overlapping any input or each other.
+ *   causal, scale, dtype : as passed to the forward pass.
+ *   workspace  : caller-owned device buffer of at least
+ *                fa_bwd_workspace_bytes(B, Nq, Hq) bytes, 16-byte aligned; its
+ *                contents on entry do not matter.
+ * Accumulation is float32; P and dS are rounded to dtype as MFMA operands.
+ * There are no atomics: the result is identical from run to run. Three
+ * kernels are enqueued on `stream` (row statistics, dK/dV, dQ).
+ * Status: FA_ERR_NULLPTR for a NULL lse, dout, dq, dk, dv or workspace,
+ * FA_ERR_WORKSPACE for a short workspace, otherwise as fa_fwd.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, int B, int Nq, int Nk, int Hq,
+                 int Hkv, int d, int causal, float scale, fa_dtype dtype, void* workspace,
+                 size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_str(fa_status status);

@@ -9,6 +9,8 @@ Contents
                      (attention_f64.c), for any shape
   backward()         fp64 gradients of that definition (dQ, dK, dV for an
                      upstream dO), written out with numpy matrix products
+  backward_magnitudes()  per gradient element, the sum of the magnitudes of
+                     the terms it adds up (the scale of its rounding error)
   mask_matrix()      the visibility rule of visible() as a boolean matrix
   brute_force()      the same definition as plain Python loops with math.fsum,
                      for tiny shapes; it cross-checks the C routine
@@ -246,3 +248,47 @@ def backward(q, k, v, do, causal=False, scale=None, window=(-1, -1)):
             dk[b, :, g] += scale * (ds.T @ qh)
             dv[b, :, g] += p.T @ doh
     return dq, dk, dv
+
+
+def backward_magnitudes(q, k, v, do, causal=False, scale=None, window=(-1, -1)):
+    """fp64 magnitudes (mq, mk, mv) of the sums behind backward()'s gradients.
+
+    Each gradient element is a sum of terms; a sum whose terms carry relative
+    errors u has an error of at most u times the sum of the terms' absolute
+    values, which is what this returns, with the row term D_i = sum_c dO O
+    counted by its own magnitude (an implementation forms D from its rounded O):
+      mv = sum_i P_ij |dO_ic|,
+      aS_ij = P_ij (|dP_ij - D_i| + sum_c |dO_ic O_ic|),
+      mq = |scale| sum_j aS_ij |K_jc|,  mk = |scale| sum_i aS_ij |Q_ic|,
+    group-summed over the query heads of a key/value head like the gradients."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    do = np.asarray(do, np.float64)
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    group = Hq // Hkv
+    vis = mask_matrix(Nq, Nk, causal, window)
+    has = vis.any(axis=1)
+    mq = np.zeros_like(q)
+    mk = np.zeros_like(k)
+    mv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            qh, kh, vh, doh = q[b, :, h], k[b, :, g], v[b, :, g], do[b, :, h]
+            s = scale * (qh @ kh.T)
+            s = np.where(vis, s, -np.inf)
+            m = np.where(has, s.max(axis=1), 0.0)
+            e = np.where(vis, np.exp(s - m[:, None]), 0.0)
+            p = e / np.where(has, e.sum(axis=1), 1.0)[:, None]
+            o = p @ vh
+            dp = doh @ vh.T
+            dd = (doh * o).sum(axis=1)
+            a_s = p * (np.abs(dp - dd[:, None]) + np.abs(doh * o).sum(axis=1)[:, None])
+            mq[b, :, h] = abs(scale) * (a_s @ np.abs(kh))
+            mk[b, :, g] += abs(scale) * (a_s.T @ np.abs(qh))
+            mv[b, :, g] += p.T @ np.abs(doh)
+    return mq, mk, mv

@@ -6,7 +6,8 @@ rounds them to the 16-bit storage formats (round to nearest, ties to even),
 returning the raw 16-bit patterns. Both sides consume the same bits.
 
 Recipe: one generator per (workload id, tensor id, batch index), so that any
-batch slice can be regenerated on its own. Tensor ids: Q=0, K=1, V=2. Values
+batch slice can be regenerated on its own. Tensor ids: Q=0, K=1, V=2, and
+dO=3 (the upstream gradient of a backward workload). Values
 are N(0,1) in float32, multiplied by ``mult`` (an exact power of two in every
 workload here), then rounded to fp16 or bf16.
 
@@ -22,7 +23,7 @@ import math
 
 import numpy as np
 
-Q_ID, K_ID, V_ID = 0, 1, 2
+Q_ID, K_ID, V_ID, DO_ID = 0, 1, 2, 3
 DTYPES = ("f16", "bf16")
 
 
@@ -114,6 +115,10 @@ class Workload:
         v = normal_bits(self.wid, V_ID, sv, self.dtype, 1.0, batches)
         return q, k, v
 
+    def grad_out(self, batches=None):
+        """dO as uint16 bits shaped like q (backward workloads)."""
+        return normal_bits(self.wid, DO_ID, self.shapes()[0], self.dtype, 1.0, batches)
+
     def pairs(self) -> int:
         """Number of unmasked (query, key) pairs per (b, head)."""
         if not self.causal:
@@ -146,6 +151,12 @@ def _build():
     for nq in (1, 8):
         w.append(Workload(f"decode_bf16_nq{nq}", wid, 8, nq, 8192, 32, 8, 128, "bf16", False,
                           decode=True, num_splits=16))
+        wid += 1
+    # backward: the pages' fwd+bwd benchmark setting at N = 4096 (hidden 2048 as
+    # 16 heads of 128, batch 16K / N = 4)
+    for causal in (False, True):
+        w.append(Workload(f"bwd_bf16_4096_{'causal' if causal else 'full'}", wid, 4, 4096, 4096, 16, 16,
+                          128, "bf16", causal))
         wid += 1
     return {x.name: x for x in w}
 

@@ -8,6 +8,16 @@ type; without it no bf16 output could meet 1e-2 where |O| >= 4 (bf16 spacing
 there is 2^-5). LSE (fp32): |LSE_gpu - LSE_ref| <= 1e-3 where finite, and both
 -inf exactly where a row sees no key.
 
+Gradients dQ, dK, dV (fp16/bf16) against the fp64 oracle, element by element:
+  |G_gpu - G_ref| - ulp(G_ref)/2 <= 2 u M
+with u the unit roundoff of the input type (2^-8 bf16, 2^-11 fp16) and M the
+sum of the magnitudes of the terms the element adds up (oracle
+backward_magnitudes). An implementation that rounds P and dS to the input type
+as MFMA operands, accumulates in fp32 and forms D from its rounded O has an
+error of at most about u M; a float32 emulation of that arithmetic reaches
+0.84 u M on the test shapes, and a dropped D term, a causal mask one key off
+or two swapped dO rows exceed the bound 3x to 10^5x.
+
 Secondary rule (the upstream test criterion: error at most twice that of a
 plain implementation): max error <= 2 * max error of a float32 emulation
 (fp32 scores and softmax, P rounded to the input type, fp32 P V, O rounded)
@@ -47,6 +57,28 @@ def check_o(o_gpu, o_ref, dtype, what=""):
     assert worst <= MAX_TOL, f"{what}: max |dO| - ulp/2 = {worst:.3g} > {MAX_TOL} {stats}"
     assert mean <= MEAN_TOL, f"{what}: mean |dO| = {mean:.3g} > {MEAN_TOL} {stats}"
     return stats
+
+
+UNIT_ROUNDOFF = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+GRAD_BOUND = 2.0
+
+
+def check_grad(g_gpu, g_ref, mag, dtype, what=""):
+    """Element-wise rounding-error bound on a gradient (rule above)."""
+    g_gpu = np.asarray(g_gpu, np.float64)
+    g_ref = np.asarray(g_ref, np.float64)
+    assert g_gpu.shape == g_ref.shape, (g_gpu.shape, g_ref.shape)
+    assert np.all(np.isfinite(g_gpu)), f"{what}: non-finite gradient"
+    excess = np.abs(g_gpu - g_ref) - 0.5 * ulp(g_ref, dtype)
+    bound = UNIT_ROUNDOFF[dtype] * np.asarray(mag, np.float64)
+    ratio = np.where(excess > 0, excess / np.maximum(bound, 1e-300), 0.0)
+    worst = float(ratio.max()) if ratio.size else 0.0
+    if worst > GRAD_BOUND:
+        i = np.unravel_index(int(ratio.argmax()), ratio.shape)
+        raise AssertionError(f"{what}: |dG| = {abs(g_gpu[i] - g_ref[i]):.3g} at {i} exceeds {GRAD_BOUND} u M "
+                             f"(u M = {bound[i]:.3g}, ref {g_ref[i]:.3g}, gpu {g_gpu[i]:.3g}); "
+                             f"ratio {worst:.3g}")
+    return worst
 
 
 def check_lse(lse_gpu, lse_ref, what=""):

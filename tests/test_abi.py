@@ -152,3 +152,29 @@ def test_fwd_varlen_rejects_invalid_arguments(lib, kw, status):
 def test_fwd_window_rejects_invalid_windows(lib, wl, wr, status):
     q = None if status == 1 else FAKE   # a valid window reaches the pointer check
     assert lib.fa_fwd_window(q, FAKE, FAKE, FAKE, FAKE, 1, 8, 8, 2, 1, 64, wl, wr, 0, 0.125, 0, None) == status
+
+
+def test_bwd_workspace_size(lib):
+    ws = lib.fa_bwd_workspace_bytes
+    # two float32 arrays [B][Hq][Nq rounded up to 32], each padded to 256 bytes
+    assert ws(2, 100, 3) == 2 * (((2 * 3 * 128 * 4) + 255) // 256 * 256)
+    assert ws(1, 1, 1) == 2 * 256
+    assert ws(0, 8, 1) == 0 and ws(1, 0, 1) == 0 and ws(1, 8, 0) == 0
+
+
+def bwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, Nq=8, Nk=8,
+        Hq=2, Hkv=1, d=64, causal=0, scale=0.125, dtype=1, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = lib.fa_bwd_workspace_bytes(B, Nq, Hq) if min(B, Nq, Hq) >= 1 else 0
+    return lib.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, B, Nq, Nk, Hq, Hkv, d, causal, scale, dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(lse=None), 1), (dict(do=None), 1), (dict(dq=None), 1),
+    (dict(dk=None), 1), (dict(dv=None), 1), (dict(ws=None), 1),
+    (dict(B=0), 2), (dict(Nk=0), 2), (dict(Hq=3, Hkv=2), 3), (dict(d=80), 4), (dict(dtype=4), 5),
+    (dict(wsb=16), 7), (dict(do=MIS), 9), (dict(dq=MIS), 9), (dict(dk=MIS), 9), (dict(dv=MIS), 9),
+    (dict(ws=MIS), 9), (dict(lse=FAKE + 2), 9), (dict(scale=float("nan")), 10),
+])
+def test_bwd_rejects_invalid_arguments(lib, kw, status):
+    assert bwd(lib, **kw) == status

@@ -374,3 +374,32 @@ def test_backward_rows_without_keys_have_zero_gradient():
     dq, dk, dv = oracle.backward(q, k, v, do, causal=True)
     # causal with Nq = 6 > Nk = 3: rows 0..2 see no key
     assert np.all(dq[0, :3] == 0) and np.all(np.isfinite(dk)) and np.all(np.isfinite(dv))
+
+
+def test_backward_magnitudes_bound_the_gradients():
+    # triangle inequality: every gradient element is at most the sum of the magnitudes
+    # of its terms, for masks, GQA and a negative scale alike
+    for causal, window, scale in [(False, (-1, -1), None), (True, (-1, -1), 0.3), (False, (2, 0), -0.5)]:
+        q, k, v, do = rand(2, 7, 4, 5), rand(2, 9, 2, 5), rand(2, 9, 2, 5), rand(2, 7, 4, 5)
+        grads = oracle.backward(q, k, v, do, causal=causal, scale=scale, window=window)
+        mags = oracle.backward_magnitudes(q, k, v, do, causal=causal, scale=scale, window=window)
+        for g, m in zip(grads, mags):
+            assert np.all(m >= 0)
+            assert np.all(np.abs(g) <= m * (1 + 1e-12) + 1e-15)
+
+
+def test_backward_magnitudes_equal_dv_for_nonnegative_do():
+    # P >= 0, so with dO >= 0 every term of dV = P^T dO is non-negative: the magnitude is dV
+    q, k, v, do = rand(1, 6, 4, 3), rand(1, 8, 2, 3), rand(1, 8, 2, 3), np.abs(rand(1, 6, 4, 3))
+    _, _, dv = oracle.backward(q, k, v, do, causal=True)
+    _, _, mv = oracle.backward_magnitudes(q, k, v, do, causal=True)
+    np.testing.assert_allclose(mv, dv, rtol=1e-13, atol=1e-15)
+
+
+def test_backward_magnitudes_are_homogeneous_in_do():
+    # every term is linear in dO (D too), so all magnitudes scale with |c|
+    q, k, v, do = rand(1, 5, 2, 4), rand(1, 6, 1, 4), rand(1, 6, 1, 4), rand(1, 5, 2, 4)
+    a = oracle.backward_magnitudes(q, k, v, do, causal=True)
+    b = oracle.backward_magnitudes(q, k, v, -3.0 * do, causal=True)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(y, 3.0 * x, rtol=1e-12)
