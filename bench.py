@@ -130,7 +130,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["fwd", "headline", "decode", "all"], default="all")
+    ap.add_argument("--only", choices=["fwd", "headline", "decode", "bwd", "all"], default="all")
     ap.add_argument("--prewarm-s", type=float, default=1.0,
                     help="seconds of untimed launches per workload before its warmup steps")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -266,6 +266,31 @@ def main():
                            "config": {"workload": wd.name}})
         del sets, ws, o, lse
         torch.cuda.empty_cache()
+
+    # ---- backward at the pages' fwd+bwd benchmark setting (N 4096, 16 heads of 128, B 4)
+    if args.only in ("bwd", "all"):
+        from exact_tiled_attention_21_amd import attention_backward, bwd_workspace_bytes
+        for name in ("bwd_bf16_4096_full", "bwd_bf16_4096_causal"):
+            wb = synthetic.WORKLOADS[name]
+            q, k, v = upload(wb, torch)
+            dt = q.dtype
+            do = torch.from_numpy(np.ascontiguousarray(wb.grad_out()).view(np.int16)).to(dev).view(dt)
+            o, lse = attention(q, k, v, causal=wb.causal, scale=wb.scale)
+            ws = torch.empty(bwd_workspace_bytes(wb.B, wb.Nq, wb.Hq), dtype=torch.uint8, device=dev)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            msb = time_steps(lambda i=0: attention_backward(q, k, v, o, lse, do, causal=wb.causal, scale=wb.scale,
+                                                            workspace=ws, dq=dq, dk=dk, dv=dv),
+                             max(5, args.steps // 5), max(2, args.warmup // 5), torch, args.prewarm_s)
+            # the pages' convention: the backward does 2.5x the forward's matrix FLOPs
+            # (five products of 2 N^2 d against two); these kernels execute seven
+            fl = 2.5 * wb.flops()
+            tb = fl / (msb * 1e-3) / 1e12
+            result["bwd_4096_" + ("causal" if wb.causal else "full")] = {
+                "workload": wb.name, "ms": round(msb, 4), "tflops": round(tb, 2),
+                "tflops_executed": round(tb * 3.5 / 2.5, 2),
+                "mfma_peak_frac": round(tb / PEAK_MFMA_F16, 4)}
+            del q, k, v, do, o, lse, ws, dq, dk, dv
+            torch.cuda.empty_cache()
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w)

@@ -137,6 +137,9 @@ fa_status fwd_common(fa::FwdArgs& a, int d, int wl, int wr, int causal, float sc
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// rows of each backward statistics array: [B][Hq][Nq rounded up to 64]
+size_t bwd_stat_rows(int B, int Nq, int Hq) { return size_t(B) * Hq * ((size_t(Nq) + 63) / 64 * 64); }
+
 }  // namespace
 
 extern "C" {
@@ -240,8 +243,7 @@ fa_status fa_decode_splitkv_paged(const void* q, const void* k_pages, const void
 
 size_t fa_bwd_workspace_bytes(int B, int Nq, int Hq) {
   if (B < 1 || Nq < 1 || Hq < 1) return 0;
-  const size_t rows = size_t(B) * Hq * ((size_t(Nq) + 31) / 32 * 32);
-  return 2 * pad256(rows * sizeof(float));
+  return 2 * pad256(bwd_stat_rows(B, Nq, Hq) * sizeof(float));
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -256,11 +258,12 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
     return FA_ERR_ALIGN;
   const int64_t nkt = (int64_t(Nk) + 127) / 128, nqt = (int64_t(Nq) + 127) / 128;
   if (nkt * Hkv * B > 0x7fffffffLL || nqt * Hq * B > 0x7fffffffLL) return FA_ERR_SHAPE;
-  if (int64_t(B) * Hq * ((int64_t(Nq) + 31) / 32 * 32) > 0x3fffffffLL) return FA_ERR_SHAPE;
+  // both statistics arrays addressed with 32-bit byte offsets
+  if (bwd_stat_rows(B, Nq, Hq) > 0x0fffffffu) return FA_ERR_SHAPE;
   fa::BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  const size_t rows = size_t(B) * Hq * ((size_t(Nq) + 31) / 32 * 32);
+  const size_t rows = bwd_stat_rows(B, Nq, Hq);
   a.dsum = static_cast<float*>(workspace);
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + pad256(rows * sizeof(float)));
   a.B = B; a.Nq = Nq; a.Nk = Nk; a.Hq = Hq; a.Hkv = Hkv;

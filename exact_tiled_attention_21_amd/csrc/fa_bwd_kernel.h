@@ -10,7 +10,7 @@
 // atomics, in three kernels:
 //   fa_bwd_pre_kernel   D per query row, and the LSE in log2 units (+inf for a
 //                       row with no visible key and for the padding rows, so
-//                       their P is exactly 0), stored [B][Hq][Nq rounded to 32];
+//                       their P is exactly 0), stored [B][Hq][Nq rounded to 64];
 //   fa_bwd_dkdv_kernel  one workgroup per 128 keys of a KV head, walking every
 //                       query head of its group and every query tile; owns dK
 //                       and dV of its keys. Orientation S = Q K^T: a lane owns a
@@ -38,18 +38,22 @@ template <int D> struct BwdCfg {
   static constexpr int NS = D / 16;                 // 16-wide d slices
   static constexpr int NCB = D / 32;                // 32-wide d blocks
   static constexpr int TILE = BT * D * 2;           // bytes of one [32][D] tile
-  static constexpr int NPIECE = TILE / 1024;        // 1 KB DMA pieces per tile
-  static constexpr int NDMA = (NPIECE + NW - 1) / NW;
-  static constexpr bool EVEN = NPIECE % NW == 0;
-  static_assert(TILE % 1024 == 0, "tile must split into whole DMA pieces");
+  static constexpr int BQ = 64;                     // query rows per step of the dK/dV pass
+  static constexpr int TILEQ = BQ * D * 2;
 };
 
-// DMA of [32][D] row tiles (row pitch `pitch` bytes) into swizzled LDS. Piece
+// DMA of [ROWS][D] row tiles (row pitch `pitch` bytes) into swizzled LDS. Piece
 // i of this wave fills LDS bytes [(i NW + wave) 1024, +1024): lane l writes the
 // 16 bytes at +16 l, physical chunk pch of row r, so it fetches logical chunk
 // pch ^ swz(r) of that row. Bytes at or past `valid` read as zero.
-template <int D> struct BwdDma {
-  using C = BwdCfg<D>;
+template <int D, int ROWS> struct BwdDma {
+  struct C {
+    static constexpr int NW = BwdCfg<D>::NW;
+    static constexpr int NPIECE = ROWS * D * 2 / 1024;   // 1 KB pieces per tile
+    static constexpr int NDMA = (NPIECE + NW - 1) / NW;
+    static constexpr bool EVEN = NPIECE % NW == 0;
+    static_assert(ROWS * D * 2 % 1024 == 0, "tile must split into whole DMA pieces");
+  };
   uint32_t goff[C::NDMA];
   int wave;
   __device__ __forceinline__ void init(uint32_t pitch, int wave_, int lane) {
@@ -72,10 +76,12 @@ template <int D> struct BwdDma {
   }
 };
 
-// Two LDS stages of two [32][D] tiles each (Q and dO, or K and V).
+// Two LDS stages of two row tiles each (Q and dO, or K and V), and for the
+// dK/dV pass the row statistics of each stage.
 struct BwdLds {
   char* x[2];
   char* y[2];
+  float* st[2];
 };
 
 // A-operand fragment of the rows of a swizzled [32][D] tile: 32 rows x d slice s.
@@ -84,12 +90,12 @@ __device__ __forceinline__ V8 row_frag(const char* t, int s, int lane) {
   return lds_read_v8<V8>(t, Swz<D>::off(lane & 31, 2u * s + (lane >> 5)));
 }
 
-// Padded row count of the per-row statistics.
-__host__ __device__ constexpr int bwd_nq_pad(int nq) { return (nq + 31) / 32 * 32; }
+// Padded row count of the per-row statistics (whole dK/dV query tiles).
+__host__ __device__ constexpr int bwd_nq_pad(int nq) { return (nq + 63) / 64 * 64; }
 
 // ---------------------------------------------------------------- preprocess
 
-// G lanes per statistics entry (b, h, i), i < Nq rounded up to 32:
+// G lanes per statistics entry (b, h, i), i < Nq rounded up to 64:
 // D = sum_c dO * O in fp32 and the LSE in log2 units; padding rows and rows
 // that saw no key get D = 0, LSE = +inf.
 template <int D, bool BF16>
@@ -144,10 +150,7 @@ template <int D, bool BF16, bool CAUSAL> struct DkdvWave {
   uint32_t qpitch;
   V8 kf[C::NS], vf[C::NS];          // this lane's key row of K and V (B operands)
   f32x16 dvt[C::NCB], dkt[C::NCB];  // dV^T and dK^T, [d][key]
-  // log2 LSE and D of the 16 query rows of this lane's accumulator registers,
-  // per stage (loaded one step ahead, with the tiles)
-  f32x4 sl[2][4], sd[2][4];
-  BwdDma<D> dma;
+  BwdDma<D, C::BQ> dma;
 
   __device__ __forceinline__ DkdvWave(const BwdArgs& args, int b_, int g_, int k0) : a(args), b(b_), g(g_) {
     lane = threadIdx.x & 63;
@@ -156,10 +159,10 @@ template <int D, bool BF16, bool CAUSAL> struct DkdvWave {
     k0w = k0 + wave * C::BT;
     key = k0w + (lane & 31);
     diag = a.Nk - a.Nq;
-    nqt = (a.Nq + C::BT - 1) / C::BT;
+    nqt = (a.Nq + C::BQ - 1) / C::BQ;
     nqp = bwd_nq_pad(a.Nq);
     // causal: query tiles before the first row that sees key k0 contribute nothing
-    t0 = CAUSAL ? min(nqt, max(0, k0 - diag) / C::BT) : 0;
+    t0 = CAUSAL ? min(nqt, max(0, k0 - diag) / C::BQ) : 0;
     qpitch = static_cast<uint32_t>(a.Hq) * D * 2;
     const size_t kv = ((static_cast<size_t>(b) * a.Nk + key) * a.Hkv + g) * D + 8 * hh;
     const T* kp = reinterpret_cast<const T*>(a.k) + kv;
@@ -177,55 +180,49 @@ template <int D, bool BF16, bool CAUSAL> struct DkdvWave {
     dma.init(qpitch, wave, lane);
   }
 
-  // Q and dO rows t*32 .. of query head hi of the group into one stage, and
-  // the statistics of those rows (rows 8 gq + 4 hh + 0..3 into sl/sd[gq])
-  __device__ __forceinline__ void fetch(int hi, int t, char* ql, char* ol, f32x4 (&l)[4], f32x4 (&dd)[4]) const {
-    const size_t si = (static_cast<size_t>(b) * a.Hq + g * a.group + hi) * nqp + t * C::BT + 4 * hh;
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      l[gq] = *reinterpret_cast<const f32x4*>(a.lse2 + si + 8 * gq);
-      dd[gq] = *reinterpret_cast<const f32x4*>(a.dsum + si + 8 * gq);
-    }
-    const size_t off = ((static_cast<size_t>(b) * a.Nq + t * C::BT) * a.Hq + g * a.group + hi) * D * 2;
-    const int64_t valid = static_cast<int64_t>(a.Nq - t * C::BT - 1) * qpitch + D * 2;
+  // Q and dO rows t*64 .. of query head hi of the group into one stage, and
+  // their statistics: the log2 LSE of the 64 rows, then their D (lanes 0..15
+  // and 16..31 of wave 0 move 16 bytes each)
+  __device__ __forceinline__ void fetch(int hi, int t, char* ql, char* ol, float* stl) const {
+    const size_t off = ((static_cast<size_t>(b) * a.Nq + t * C::BQ) * a.Hq + g * a.group + hi) * D * 2;
+    const int64_t valid = static_cast<int64_t>(a.Nq - t * C::BQ - 1) * qpitch + D * 2;
     dma.issue(reinterpret_cast<const char*>(a.q) + off, valid, ql);
     dma.issue(reinterpret_cast<const char*>(a.dout) + off, valid, ol);
+    if (wave == 0 && lane < 32) {
+      const uint32_t lse_off = static_cast<uint32_t>(reinterpret_cast<const char*>(a.lse2) -
+                                                     reinterpret_cast<const char*>(a.dsum));
+      const uint32_t row0 = ((b * a.Hq + g * a.group + hi) * nqp + t * C::BQ + 4 * (lane & 15)) * 4;
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          a.dsum, 0, lse_off + static_cast<uint32_t>(a.B * a.Hq * nqp) * 4, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)stl, 16,
+                                               (lane < 16 ? lse_off : 0u) + row0, 0, 0, 0);
+    }
   }
 
-  // Tile t of query head hi (stage ST): S = Q K^T and dP = dO V^T with the query
-  // rows in registers (row q0 + 8 (r / 4) + 4 hh + r % 4 in register r), then
-  // dV^T += dO^T P and dK^T += Q^T dS over those rows. The transposed tiles
-  // come from v_frag, whose row order matches the one the accumulator gives P
-  // and dS as B operands. The next tile (in head-major order) is fetched first.
-  template <int ST, bool MASK>
-  __device__ __forceinline__ void step(int hi, int t, const BwdLds& lds) {
-    {
-      int hn = hi, tn = t + 1;
-      if (tn == nqt) {
-        hn = hi + 1;
-        tn = t0;
-      }
-      if (hn < a.group) fetch(hn, tn, lds.x[ST ^ 1], lds.y[ST ^ 1], sl[ST ^ 1], sd[ST ^ 1]);
-    }
-    const char* qt = lds.x[ST];
-    const char* ot = lds.y[ST];
-    const int q0 = t * C::BT;
-    f32x16 s = f32x16{}, dp = f32x16{};
+  // The 32 query rows from q0 of one half of a tile (tiles qt, ot in LDS, S and
+  // dP already computed): P and dS with the query rows in registers (row
+  // q0 + 8 (r / 4) + 4 hh + r % 4 in register r), then dV^T += dO^T P and
+  // dK^T += Q^T dS over those rows. The transposed tiles come from v_frag, whose
+  // row order matches the one the accumulator gives P and dS as B operands.
+  template <bool MASK>
+  __device__ __forceinline__ void half(int q0, const char* qt, const char* ot, const float* stl,
+                                       const f32x16& s, const f32x16& dp) {
+    f32x4 l4[4], d4[4];
 #pragma unroll
-    for (int i = 0; i < C::NS; ++i) {
-      s = E::mfma(row_frag<D, V8>(qt, i, lane), kf[i], s);
-      dp = E::mfma(row_frag<D, V8>(ot, i, lane), vf[i], dp);
+    for (int gq = 0; gq < 4; ++gq) {
+      l4[gq] = *reinterpret_cast<const f32x4*>(stl + 8 * gq + 4 * hh);
+      d4[gq] = *reinterpret_cast<const f32x4*>(stl + C::BQ + 8 * gq + 4 * hh);
     }
     f32x16 p, ds;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float pr = exp2_fast(__builtin_fmaf(s[r], a.sl2, -sl[ST][r >> 2][r & 3]));
+      float pr = exp2_fast(__builtin_fmaf(s[r], a.sl2, -l4[r >> 2][r & 3]));
       if (MASK) {
         const int q = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
         pr = (key > q + diag) ? 0.f : pr;
       }
       p[r] = pr;
-      ds[r] = pr * (dp[r] - sd[ST][r >> 2][r & 3]);
+      ds[r] = pr * (dp[r] - d4[r >> 2][r & 3]);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -237,6 +234,39 @@ template <int D, bool BF16, bool CAUSAL> struct DkdvWave {
         dkt[cb] = E::mfma(v_frag<D, V8>(qt, cb, u, lane), dsf, dkt[cb]);
       }
     }
+  }
+
+  // Tile t (64 query rows) of query head hi, in stage ST: S = Q K^T and
+  // dP = dO V^T for both 32-row halves first, so that the exponentials of one
+  // half can overlap the products of the other. The next tile (in head-major
+  // order) is fetched first.
+  template <int ST, bool MASK>
+  __device__ __forceinline__ void step(int hi, int t, const BwdLds& lds) {
+    {
+      int hn = hi, tn = t + 1;
+      if (tn == nqt) {
+        hn = hi + 1;
+        tn = t0;
+      }
+      if (hn < a.group) fetch(hn, tn, lds.x[ST ^ 1], lds.y[ST ^ 1], lds.st[ST ^ 1]);
+    }
+    const char* qt = lds.x[ST];
+    const char* ot = lds.y[ST];
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      s[h2] = f32x16{};
+      dp[h2] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < C::NS; ++i) {
+        s[h2] = E::mfma(row_frag<D, V8>(qt + h2 * C::TILE, i, lane), kf[i], s[h2]);
+        dp[h2] = E::mfma(row_frag<D, V8>(ot + h2 * C::TILE, i, lane), vf[i], dp[h2]);
+      }
+    }
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+      half<MASK>(t * C::BQ + h2 * C::BT, qt + h2 * C::TILE, ot + h2 * C::TILE, lds.st[ST] + h2 * C::BT,
+                 s[h2], dp[h2]);
     __syncthreads();
   }
 
@@ -285,29 +315,39 @@ template <int D, bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(BwdCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fa_bwd_dkdv_kernel(const BwdArgs a) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char q_lds0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char q_lds1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char o_lds0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char o_lds1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char q_lds0[C::TILEQ];
+  __shared__ __attribute__((aligned(1024))) char q_lds1[C::TILEQ];
+  __shared__ __attribute__((aligned(1024))) char o_lds0[C::TILEQ];
+  __shared__ __attribute__((aligned(1024))) char o_lds1[C::TILEQ];
+  __shared__ __attribute__((aligned(16))) float st_lds0[2 * C::BQ];
+  __shared__ __attribute__((aligned(16))) float st_lds1[2 * C::BQ];
 
   const int nkt = (a.Nk + C::WROWS - 1) / C::WROWS;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int kt = bid % nkt;
-  const int gb = bid / nkt;
+  int kt, gb;
+  if (CAUSAL) {
+    // the first key tiles see the most query rows: dispatch them first, head
+    // fastest, so each XCD (workgroup id mod 8) keeps the heads id = x mod 8
+    kt = blockIdx.x / (a.Hkv * a.B);
+    gb = blockIdx.x % (a.Hkv * a.B);
+  } else {
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    kt = bid % nkt;
+    gb = bid / nkt;
+  }
   const int g = gb % a.Hkv;
   const int b = gb / a.Hkv;
   const int k0 = kt * C::WROWS;
   DkdvWave<D, BF16, CAUSAL> w(a, b, g, k0);
-  const BwdLds lds{{q_lds0, q_lds1}, {o_lds0, o_lds1}};
+  const BwdLds lds{{q_lds0, q_lds1}, {o_lds0, o_lds1}, {st_lds0, st_lds1}};
 
   // causal: tiles [t0, tm) hold rows for which some key of the workgroup is
   // masked (the diagonal); later tiles see every key of it
   int tm = w.t0;
   if (CAUSAL) {
     const int x = k0 + C::WROWS - w.diag;   // first row that sees every key
-    tm = min(w.nqt, max(w.t0, x > 0 ? (x + C::BT - 1) / C::BT : 0));
+    tm = min(w.nqt, max(w.t0, x > 0 ? (x + C::BQ - 1) / C::BQ : 0));
   }
-  if (w.t0 < w.nqt) w.fetch(0, w.t0, lds.x[0], lds.y[0], w.sl[0], w.sd[0]);
+  if (w.t0 < w.nqt) w.fetch(0, w.t0, lds.x[0], lds.y[0], lds.st[0]);
   __syncthreads();
   int n = 0;
   for (int hi = 0; hi < a.group && w.t0 < w.nqt; ++hi) {
@@ -336,7 +376,7 @@ template <int D, bool BF16, bool CAUSAL> struct DqWave {
   int nsteps;
   V8 qf[C::NS], of[C::NS];   // this lane's query row of Q and dO (B operands)
   f32x16 dqt[C::NCB];        // dQ^T, [d][q]
-  BwdDma<D> dma;
+  BwdDma<D, C::BT> dma;
 
   __device__ __forceinline__ DqWave(const BwdArgs& args, int b_, int hq_, int q0) : a(args), b(b_), hq(hq_) {
     lane = threadIdx.x & 63;
@@ -438,7 +478,7 @@ template <int D, bool BF16, bool CAUSAL> struct DqWave {
 };
 
 template <int D, bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(BwdCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(BwdCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1, D <= 128 ? 2 : 1)))
 void fa_bwd_dq_kernel(const BwdArgs a) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) char k_lds0[C::TILE];
@@ -447,15 +487,21 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char v_lds1[C::TILE];
 
   const int nqt = (a.Nq + C::WROWS - 1) / C::WROWS;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  int qt = bid % nqt;
-  const int hb = bid / nqt;
+  int qt, hb;
+  if (CAUSAL) {
+    // the last query tiles see the most keys: dispatch them first, head fastest
+    qt = nqt - 1 - static_cast<int>(blockIdx.x / (a.Hq * a.B));
+    hb = blockIdx.x % (a.Hq * a.B);
+  } else {
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    qt = bid % nqt;
+    hb = bid / nqt;
+  }
   const int hq = hb % a.Hq;
   const int b = hb / a.Hq;
-  if (CAUSAL) qt = nqt - 1 - qt;   // longest rows first
   const int q0 = qt * C::WROWS;
   DqWave<D, BF16, CAUSAL> w(a, b, hq, q0);
-  const BwdLds lds{{k_lds0, k_lds1}, {v_lds0, v_lds1}};
+  const BwdLds lds{{k_lds0, k_lds1}, {v_lds0, v_lds1}, {nullptr, nullptr}};
 
   // key tiles the workgroup needs (causal: up to its last row's diagonal), and
   // the first one where some row needs an element mask (key tail, diagonal)

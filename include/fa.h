@@ -195,7 +195,7 @@ fa_status fa_decode_splitkv_paged(const void* q, const void* k_pages, const void
 
 /*
  * Bytes of device workspace fa_bwd needs: two float32 arrays [B][Hq][Nq'] with
- * Nq' = Nq rounded up to a multiple of 32, each padded to 256 bytes. Returns 0
+ * Nq' = Nq rounded up to a multiple of 64, each padded to 256 bytes. Returns 0
  * for invalid sizes.
  */
 size_t fa_bwd_workspace_bytes(int B, int Nq, int Hq);
@@ -222,7 +222,8 @@ size_t fa_bwd_workspace_bytes(int B, int Nq, int Hq);
  * There are no atomics: the result is identical from run to run. Three
  * kernels are enqueued on `stream` (row statistics, dK/dV, dQ).
  * Status: FA_ERR_NULLPTR for a NULL lse, dout, dq, dk, dv or workspace,
- * FA_ERR_WORKSPACE for a short workspace, otherwise as fa_fwd.
+ * FA_ERR_WORKSPACE for a short workspace, FA_ERR_SHAPE when B * Hq * Nq'
+ * exceeds 2^28 - 1, otherwise as fa_fwd.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                  const void* dout, void* dq, void* dk, void* dv, int B, int Nq, int Nk, int Hq,
