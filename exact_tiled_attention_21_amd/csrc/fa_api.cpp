@@ -132,6 +132,9 @@ fa_status fwd_common(fa::FwdArgs& a, int d, int wl, int wr, int causal, float sc
   a.wr = causal ? 0 : wr;
   const int64_t blocks = int64_t(a.n_qtiles) * a.Hq * a.B;
   if (blocks > 0x7fffffff) return FA_ERR_SHAPE;
+  // K and V bytes each query head reads (a group shares them)
+  const int64_t kv_rows = a.cu_k ? int64_t(a.total_k) / a.B : a.Nk;
+  a.hb = fa::order_block_heads(int64_t(a.Hq) * a.B, kv_rows * d * 4 / a.group);
   const bool band = a.wl >= 0 || a.wr >= 0;
   hipError_t e = fa::launch_fwd(a, d, dtype == FA_BF16, band, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -270,6 +273,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   a.group = Hq / Hkv;
   a.sl2 = scale * 1.4426950408889634f;
   a.scale = scale;
+  a.hb_kv = fa::order_block_heads(int64_t(Hkv) * B, int64_t(a.group) * Nq * d * 4);   // Q and dO of a group
+  a.hb_q = fa::order_block_heads(int64_t(Hq) * B, int64_t(Nk) * d * 4 / a.group);     // K and V per query head
   hipError_t e = fa::launch_bwd(a, d, dtype == FA_BF16, causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

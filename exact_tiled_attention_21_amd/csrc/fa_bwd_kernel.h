@@ -325,10 +325,8 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
   const int nkt = (a.Nk + C::WROWS - 1) / C::WROWS;
   int kt, gb;
   if (CAUSAL) {
-    // the first key tiles see the most query rows: dispatch them first, head
-    // fastest, so each XCD (workgroup id mod 8) keeps the heads id = x mod 8
-    kt = blockIdx.x / (a.Hkv * a.B);
-    gb = blockIdx.x % (a.Hkv * a.B);
+    // the first key tiles see the most query rows
+    blocked_order(blockIdx.x, nkt, a.Hkv * a.B, a.hb_kv, kt, gb);
   } else {
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
     kt = bid % nkt;
@@ -489,9 +487,10 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
   const int nqt = (a.Nq + C::WROWS - 1) / C::WROWS;
   int qt, hb;
   if (CAUSAL) {
-    // the last query tiles see the most keys: dispatch them first, head fastest
-    qt = nqt - 1 - static_cast<int>(blockIdx.x / (a.Hq * a.B));
-    hb = blockIdx.x % (a.Hq * a.B);
+    // the last query tiles see the most keys
+    int o;
+    blocked_order(blockIdx.x, nqt, a.Hq * a.B, a.hb_q, o, hb);
+    qt = nqt - 1 - o;
   } else {
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
     qt = bid % nqt;

@@ -156,4 +156,19 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return (bid & 7) * per + (bid >> 3);
 }
 
+// Work order for masks that make tile workloads uneven (causal). Workgroup ids
+// go to the heads in blocks of hb heads (the host sizes a block so that its
+// operands stay resident in the last-level cache); inside a block the tiles
+// come heaviest first, with the head varying fastest, so the ids on one XCD
+// (id mod 8) keep revisiting the same heads and the machine drains on light
+// tiles. `order` 0 is the heaviest tile; the caller maps it to a tile index.
+__device__ __forceinline__ void blocked_order(int p, int ntiles, int nheads, int hb, int& order, int& head) {
+  const int per_block = hb * ntiles;
+  const int blk = p / per_block;
+  const int r = p - blk * per_block;
+  const int cnt = min(hb, nheads - blk * hb);
+  order = r / cnt;
+  head = blk * hb + (r - order * cnt);
+}
+
 }  // namespace fa

@@ -377,12 +377,19 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fa_fwd
   __shared__ __attribute__((aligned(1024))) char v_lds1[C::TILE_BYTES];
 
   // workgroup -> (query tile, head, batch)
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  int qt = bid % a.n_qtiles;
-  const int hb = bid / a.n_qtiles;
+  int qt, hb;
+  if (BAND) {
+    // with a causal band the last query tiles see the most keys
+    int o;
+    blocked_order(blockIdx.x, a.n_qtiles, a.Hq * a.B, a.hb, o, hb);
+    qt = a.n_qtiles - 1 - o;
+  } else {
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    qt = bid % a.n_qtiles;
+    hb = bid / a.n_qtiles;
+  }
   const int hq = hb % a.Hq;
   const int b = hb / a.Hq;
-  if (BAND) qt = a.n_qtiles - 1 - qt;  // with a causal band: longest rows first
   const int g = hq / a.group;
 
   // the sequence: a padded batch element, or one packed sequence whose bounds

@@ -26,6 +26,7 @@ struct FwdArgs {
   const int* cu_q;
   const int* cu_k;
   int total_q, total_k;
+  int hb;          // heads per block of the heaviest-first order used with a band
 };
 
 struct DecodeArgs {
@@ -66,7 +67,17 @@ struct BwdArgs {
   int group;         // Hq / Hkv
   float sl2;         // scale * log2(e)
   float scale;
+  int hb_kv, hb_q;   // heads per block of the heaviest-first causal orders (dK/dV, dQ)
 };
+
+// Heads per block for blocked_order: as many (batch, head) pairs as keep
+// `bytes_per_head` of operands within 64 MiB, a multiple of 8 (one per XCD) when
+// there are at least 8.
+inline int order_block_heads(long long nheads, long long bytes_per_head) {
+  long long hb = (64ll << 20) / (bytes_per_head > 0 ? bytes_per_head : 1);
+  hb = hb < 8 ? 8 : hb / 8 * 8;
+  return static_cast<int>(hb < nheads ? hb : nheads);
+}
 
 // Rows of queries one forward workgroup covers (32 per wave).
 constexpr int fwd_rows(int) { return 128; }
