@@ -205,14 +205,8 @@ template <int D, bool BF16, bool CAUSAL> struct DkdvWave {
   // dK^T += Q^T dS over those rows. The transposed tiles come from v_frag, whose
   // row order matches the one the accumulator gives P and dS as B operands.
   template <bool MASK>
-  __device__ __forceinline__ void half(int q0, const char* qt, const char* ot, const float* stl,
-                                       const f32x16& s, const f32x16& dp) {
-    f32x4 l4[4], d4[4];
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      l4[gq] = *reinterpret_cast<const f32x4*>(stl + 8 * gq + 4 * hh);
-      d4[gq] = *reinterpret_cast<const f32x4*>(stl + C::BQ + 8 * gq + 4 * hh);
-    }
+  __device__ __forceinline__ void half(int q0, const char* qt, const char* ot, const f32x4 (&l4)[4],
+                                       const f32x4 (&d4)[4], const f32x16& s, const f32x16& dp) {
     f32x16 p, ds;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -224,15 +218,60 @@ template <int D, bool BF16, bool CAUSAL> struct DkdvWave {
       p[r] = pr;
       ds[r] = pr * (dp[r] - d4[r >> 2][r & 3]);
     }
+    const V8 pf[2] = {to_v8<BF16>(p, 0), to_v8<BF16>(p, 8)};
+    const V8 dsf[2] = {to_v8<BF16>(ds, 0), to_v8<BF16>(ds, 8)};
+    // MFMA m: key slice u = m / (2 NCB), d block cb = (m / 2) % NCB, dV (even m,
+    // dO^T fragment) or dK (odd m, Q^T fragment); fragments kTrPre MFMAs ahead
+    V8 fr[kTrPre];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const V8 pf = to_v8<BF16>(p, 8 * u);
-      const V8 dsf = to_v8<BF16>(ds, 8 * u);
+    for (int m = 0; m < kTrPre; ++m) fr[m] = tr_frag(qt, ot, m);
 #pragma unroll
-      for (int cb = 0; cb < C::NCB; ++cb) {
-        dvt[cb] = E::mfma(v_frag<D, V8>(ot, cb, u, lane), pf, dvt[cb]);
-        dkt[cb] = E::mfma(v_frag<D, V8>(qt, cb, u, lane), dsf, dkt[cb]);
-      }
+    for (int m = 0; m < kTrMf; ++m) {
+      const int u = m / (2 * C::NCB), cb = (m / 2) % C::NCB;
+      if (m & 1) dkt[cb] = E::mfma(fr[m % kTrPre], dsf[u], dkt[cb]);
+      else dvt[cb] = E::mfma(fr[m % kTrPre], pf[u], dvt[cb]);
+      if (m + kTrPre < kTrMf) fr[m % kTrPre] = tr_frag(qt, ot, m + kTrPre);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kTrPre, 0);
+#pragma unroll
+    for (int m = 0; m < kTrMf; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (m + kTrPre < kTrMf) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  }
+  static constexpr int kTrMf = 4 * C::NCB;
+  static constexpr int kTrPre = 3;
+  __device__ __forceinline__ V8 tr_frag(const char* qt, const char* ot, int m) const {
+    return v_frag<D, V8>((m & 1) ? qt : ot, (m / 2) % C::NCB, m / (2 * C::NCB), lane);
+  }
+
+  // S = Q K^T and dP = dO V^T for both 32-row halves of a tile: MFMA m takes
+  // the Q (even m) or dO (odd m) fragment of half m / (2 NS), d slice
+  // (m / 2) % NS. Fragments are read kPre MFMAs ahead through a rolling buffer,
+  // and the order is pinned for the scheduler, which otherwise issues each
+  // read right before its MFMA when registers are tight.
+  static constexpr int kSdMf = 4 * C::NS;
+  static constexpr int kPre = 4;
+  __device__ __forceinline__ V8 sd_frag(const char* qt, const char* ot, int m) const {
+    return row_frag<D, V8>(((m & 1) ? ot : qt) + (m / (2 * C::NS)) * C::TILE, (m / 2) % C::NS, lane);
+  }
+  __device__ __forceinline__ void sdp(const char* qt, const char* ot, f32x16 (&s)[2], f32x16 (&dp)[2]) const {
+    s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+    V8 fr[kPre];
+#pragma unroll
+    for (int m = 0; m < kPre; ++m) fr[m] = sd_frag(qt, ot, m);
+#pragma unroll
+    for (int m = 0; m < kSdMf; ++m) {
+      const int h2 = m / (2 * C::NS), i = (m / 2) % C::NS;
+      if (m & 1) dp[h2] = E::mfma(fr[m % kPre], vf[i], dp[h2]);
+      else s[h2] = E::mfma(fr[m % kPre], kf[i], s[h2]);
+      if (m + kPre < kSdMf) fr[m % kPre] = sd_frag(qt, ot, m + kPre);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+#pragma unroll
+    for (int m = 0; m < kSdMf; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (m + kPre < kSdMf) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   }
 
@@ -252,21 +291,22 @@ template <int D, bool BF16, bool CAUSAL> struct DkdvWave {
     }
     const char* qt = lds.x[ST];
     const char* ot = lds.y[ST];
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      s[h2] = f32x16{};
-      dp[h2] = f32x16{};
-#pragma unroll
-      for (int i = 0; i < C::NS; ++i) {
-        s[h2] = E::mfma(row_frag<D, V8>(qt + h2 * C::TILE, i, lane), kf[i], s[h2]);
-        dp[h2] = E::mfma(row_frag<D, V8>(ot + h2 * C::TILE, i, lane), vf[i], dp[h2]);
-      }
-    }
+    // statistics of rows 32 h2 + 8 gq + 4 hh + 0..3, read before the pinned
+    // phases so that only fragment reads are left for them to order
+    f32x4 l4[2][4], d4[2][4];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
-      half<MASK>(t * C::BQ + h2 * C::BT, qt + h2 * C::TILE, ot + h2 * C::TILE, lds.st[ST] + h2 * C::BT,
-                 s[h2], dp[h2]);
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        l4[h2][gq] = *reinterpret_cast<const f32x4*>(lds.st[ST] + h2 * C::BT + 8 * gq + 4 * hh);
+        d4[h2][gq] = *reinterpret_cast<const f32x4*>(lds.st[ST] + C::BQ + h2 * C::BT + 8 * gq + 4 * hh);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s[2], dp[2];
+    sdp(qt, ot, s, dp);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+      half<MASK>(t * C::BQ + h2 * C::BT, qt + h2 * C::TILE, ot + h2 * C::TILE, l4[h2], d4[h2], s[h2], dp[h2]);
     __syncthreads();
   }
 
@@ -413,17 +453,34 @@ template <int D, bool BF16, bool CAUSAL> struct DqWave {
 
   // Key tile j (stage ST): S^T = K Q^T and dP^T = V dO^T with the keys in
   // registers (key 32 j + 8 (r / 4) + 4 hh + r % 4 in register r), then
-  // dQ^T += K^T dS^T. The next key tile is fetched first.
+  // dQ^T += K^T dS^T. The next key tile is fetched first. As in the dK/dV pass,
+  // fragments are read a few MFMAs ahead and the order is pinned.
+  static constexpr int kSdMf = 2 * C::NS;     // MFMA m: K (even) or V (odd) rows, d slice m / 2
+  static constexpr int kPre = 4;
+  static constexpr int kTrMf = 2 * C::NCB;    // MFMA m: key slice m / NCB, d block m % NCB
+  static constexpr int kTrPre = 3;
   template <int ST, bool MASK>
   __device__ __forceinline__ void step(int j, const BwdLds& lds) {
     if (j + 1 < nsteps) fetch(j + 1, lds.x[ST ^ 1], lds.y[ST ^ 1]);
     const char* kt = lds.x[ST];
     const char* vt = lds.y[ST];
     f32x16 s = f32x16{}, dp = f32x16{};
+    {
+      V8 fr[kPre];
 #pragma unroll
-    for (int i = 0; i < C::NS; ++i) {
-      s = E::mfma(row_frag<D, V8>(kt, i, lane), qf[i], s);
-      dp = E::mfma(row_frag<D, V8>(vt, i, lane), of[i], dp);
+      for (int m = 0; m < kPre; ++m) fr[m] = row_frag<D, V8>((m & 1) ? vt : kt, m / 2, lane);
+#pragma unroll
+      for (int m = 0; m < kSdMf; ++m) {
+        if (m & 1) dp = E::mfma(fr[m % kPre], of[m / 2], dp);
+        else s = E::mfma(fr[m % kPre], qf[m / 2], s);
+        if (m + kPre < kSdMf) fr[m % kPre] = row_frag<D, V8>(((m + kPre) & 1) ? vt : kt, (m + kPre) / 2, lane);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+#pragma unroll
+      for (int m = 0; m < kSdMf; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (m + kPre < kSdMf) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
     f32x16 ds;
 #pragma unroll
@@ -436,11 +493,22 @@ template <int D, bool BF16, bool CAUSAL> struct DqWave {
       }
       ds[r] = pr * (dp[r] - dsum);
     }
+    const V8 dsf[2] = {to_v8<BF16>(ds, 0), to_v8<BF16>(ds, 8)};
+    {
+      V8 fr[kTrPre];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const V8 dsf = to_v8<BF16>(ds, 8 * u);
+      for (int m = 0; m < kTrPre; ++m) fr[m] = v_frag<D, V8>(kt, m % C::NCB, m / C::NCB, lane);
 #pragma unroll
-      for (int cb = 0; cb < C::NCB; ++cb) dqt[cb] = E::mfma(v_frag<D, V8>(kt, cb, u, lane), dsf, dqt[cb]);
+      for (int m = 0; m < kTrMf; ++m) {
+        dqt[m % C::NCB] = E::mfma(fr[m % kTrPre], dsf[m / C::NCB], dqt[m % C::NCB]);
+        if (m + kTrPre < kTrMf) fr[m % kTrPre] = v_frag<D, V8>(kt, (m + kTrPre) % C::NCB, (m + kTrPre) / C::NCB, lane);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kTrPre, 0);
+#pragma unroll
+      for (int m = 0; m < kTrMf; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (m + kTrPre < kTrMf) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
     }
     __syncthreads();
   }
