@@ -124,6 +124,22 @@ def cpu_baseline(w, budget_s=12.0):
                       f"({took:.1f} s)", "seconds": took}
 
 
+def cpu_baseline_decode(w, reps_budget_s=3.0):
+    """The oracle on the whole decode workload (all batches, heads and keys), repeated
+    for about reps_budget_s; reported as microseconds per decode step."""
+    import oracle
+    oracle.build(force=False)
+    q, k, v = [oracle.widen(x, w.dtype) for x in w.inputs()]
+    took, reps = 0.0, 0
+    while took < reps_budget_s or reps == 0:
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, causal=w.causal, scale=w.scale)
+        took += time.perf_counter() - t0
+        reps += 1
+    return {"value": round(took / reps * 1e6, 1), "unit": "us/step", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": f"{w.name}: the whole step x{reps}, fp64 ({took:.1f} s)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,10 +251,18 @@ def main():
 
         msd = time_steps(dstep, max(args.steps, 100), args.warmup, torch, args.prewarm_s)
         kv_bytes = 2 * wd.B * wd.Nk * wd.Hkv * wd.d * 2
+        # a plain device-to-device copy of 1 GiB in the same run: the attainable HBM rate
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        msc = time_steps(lambda i=0: dst.copy_(src), 10, 2, torch, 0.2)
+        copy_gbps = 2 * src.numel() / (msc * 1e-3) / 1e9   # read + write
+        del src, dst
         result["decode"] = {"workload": wd.name, "us_per_step": round(msd * 1e3, 2),
                             "kv_GBps": round(kv_bytes / (msd * 1e-3) / 1e9, 1),
                             "hbm_peak_frac": round(kv_bytes / (msd * 1e-3) / 1e9 / PEAK_HBM, 4),
                             "roofline_us": round(kv_bytes / (PEAK_HBM * 1e9) * 1e6, 2),
+                            "copy_GBps": round(copy_gbps, 1),
+                            "copy_frac": round(kv_bytes / (msd * 1e-3) / 1e9 / copy_gbps, 4),
                             "kv_sets_rotated": len(sets)}
         # the same step over a paged cache: 256-key pages in a scrambled block table
         from exact_tiled_attention_21_amd import decode_paged
@@ -294,6 +318,8 @@ def main():
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w)
+        if args.only in ("decode", "all"):
+            result["cpu_baseline_decode"] = cpu_baseline_decode(synthetic.WORKLOADS["decode_bf16_nq1"])
     print(json.dumps(result), flush=True)
     return 0
 
