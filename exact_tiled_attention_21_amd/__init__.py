@@ -9,8 +9,9 @@ kernels of libfa.so. torch supplies device memory and the current stream.
   decode(q, k_cache, v_cache, num_splits=16, scale=None, causal=False) -> (o, lse)
   decode_paged(q, k_pages, v_pages, block_table, cache_seqlens, num_splits=16,
                scale=None, causal=False) -> (o, lse)
-  attention_backward(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
-  attention_func(q, k, v, causal=False, scale=None) -> o, differentiable
+  attention_backward(q, k, v, o, lse, dout, causal=False, scale=None,
+                     window=(-1, -1)) -> (dq, dk, dv)
+  attention_func(q, k, v, causal=False, scale=None, window=(-1, -1)) -> o, differentiable
 
 Tensors are [batch, seq_len, heads, head_dim], fp16 or bf16, contiguous, on a
 ROCm device; lse is float32 [batch, heads, seq_len_q]. The default scale is
@@ -202,9 +203,9 @@ def bwd_workspace_bytes(B: int, Nq: int, Hq: int) -> int:
 
 
 def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
-                       workspace=None, dq=None, dk=None, dv=None):
-    """Gradients (dq, dk, dv) of attention(q, k, v, causal, scale) for the upstream
-    gradient dout, from the forward's output o and lse (float32 [B, Hq, Nq])."""
+                       workspace=None, dq=None, dk=None, dv=None, window=(-1, -1)):
+    """Gradients (dq, dk, dv) of attention(q, k, v, causal, scale, window=window) for the
+    upstream gradient dout, from the forward's output o and lse (float32 [B, Hq, Nq])."""
     torch = _torch()
     _check(q, k, v)
     for name, t in (("o", o), ("dout", dout)):
@@ -224,10 +225,17 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     with torch.cuda.device(q.device):
-        st = load().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                           dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Nq, Nk, Hq, Hkv, d,
-                           int(bool(causal)), float(scale), _dtype_code(q), workspace.data_ptr(),
-                           workspace.numel() * workspace.element_size(), _stream(q))
+        if tuple(window) == (-1, -1):
+            st = load().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                               dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Nq, Nk, Hq, Hkv,
+                               d, int(bool(causal)), float(scale), _dtype_code(q), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream(q))
+        else:
+            st = load().fa_bwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                      dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Nq, Nk,
+                                      Hq, Hkv, d, int(window[0]), int(window[1]), int(bool(causal)),
+                                      float(scale), _dtype_code(q), workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(), _stream(q))
     if st != 0:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
@@ -238,18 +246,18 @@ def _autograd_function():
 
     class _Attention(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, causal, scale):
-            o, lse = attention(q, k, v, causal=causal, scale=scale)
+        def forward(ctx, q, k, v, causal, scale, window):
+            o, lse = attention(q, k, v, causal=causal, scale=scale, window=window)
             ctx.save_for_backward(q, k, v, o, lse)
-            ctx.causal, ctx.scale = causal, scale
+            ctx.causal, ctx.scale, ctx.window = causal, scale, window
             return o
 
         @staticmethod
         def backward(ctx, dout):
             q, k, v, o, lse = ctx.saved_tensors
             dq, dk, dv = attention_backward(q, k, v, o, lse, dout.contiguous(), causal=ctx.causal,
-                                            scale=ctx.scale)
-            return dq, dk, dv, None, None
+                                            scale=ctx.scale, window=ctx.window)
+            return dq, dk, dv, None, None, None
 
     return _Attention
 
@@ -257,11 +265,11 @@ def _autograd_function():
 _ATTN_FN = None
 
 
-def attention_func(q, k, v, causal: bool = False, scale: float | None = None):
+def attention_func(q, k, v, causal: bool = False, scale: float | None = None, window=(-1, -1)):
     """attention(...)[0] as a differentiable torch op (forward and backward in libfa)."""
     global _ATTN_FN
     if _ATTN_FN is None:
         _ATTN_FN = _autograd_function()
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
-    return _ATTN_FN.apply(q, k, v, bool(causal), float(scale))
+    return _ATTN_FN.apply(q, k, v, bool(causal), float(scale), tuple(int(x) for x in window))

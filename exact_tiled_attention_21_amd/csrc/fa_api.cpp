@@ -50,14 +50,14 @@ hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, bool causal, hip
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool causal, hipStream_t s) {
+hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool band, hipStream_t s) {
   switch (d) {
-    case 32: return launch_bwd_d32(a, bf16, causal, s);
-    case 64: return launch_bwd_d64(a, bf16, causal, s);
-    case 96: return launch_bwd_d96(a, bf16, causal, s);
-    case 128: return launch_bwd_d128(a, bf16, causal, s);
-    case 192: return launch_bwd_d192(a, bf16, causal, s);
-    case 256: return launch_bwd_d256(a, bf16, causal, s);
+    case 32: return launch_bwd_d32(a, bf16, band, s);
+    case 64: return launch_bwd_d64(a, bf16, band, s);
+    case 96: return launch_bwd_d96(a, bf16, band, s);
+    case 128: return launch_bwd_d128(a, bf16, band, s);
+    case 192: return launch_bwd_d192(a, bf16, band, s);
+    case 256: return launch_bwd_d256(a, bf16, band, s);
   }
   return hipErrorInvalidValue;
 }
@@ -253,9 +253,18 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  const void* dout, void* dq, void* dk, void* dv, int B, int Nq, int Nk, int Hq,
                  int Hkv, int d, int causal, float scale, fa_dtype dtype, void* workspace,
                  size_t workspace_bytes, void* stream) {
+  return fa_bwd_window(q, k, v, o, lse, dout, dq, dk, dv, B, Nq, Nk, Hq, Hkv, d, -1, -1, causal, scale,
+                       dtype, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, int B, int Nq, int Nk, int Hq,
+                        int Hkv, int d, int window_left, int window_right, int causal, float scale,
+                        fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
   fa_status st = check_common(q, k, v, const_cast<void*>(o), lse, B, Nq, Nk, Hq, Hkv, d, scale, dtype);
   if (st != FA_OK) return st;
   if (!lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_NULLPTR;
+  if (window_left < -1 || window_right < -1) return FA_ERR_SHAPE;
   if (workspace_bytes < fa_bwd_workspace_bytes(B, Nq, Hq)) return FA_ERR_WORKSPACE;
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
     return FA_ERR_ALIGN;
@@ -273,9 +282,12 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   a.group = Hq / Hkv;
   a.sl2 = scale * 1.4426950408889634f;
   a.scale = scale;
+  a.wl = window_left;
+  a.wr = causal ? 0 : window_right;
   a.hb_kv = fa::order_block_heads(int64_t(Hkv) * B, int64_t(a.group) * Nq * d * 4);   // Q and dO of a group
   a.hb_q = fa::order_block_heads(int64_t(Hq) * B, int64_t(Nk) * d * 4 / a.group);     // K and V per query head
-  hipError_t e = fa::launch_bwd(a, d, dtype == FA_BF16, causal != 0, static_cast<hipStream_t>(stream));
+  const bool band = a.wl >= 0 || a.wr >= 0;
+  hipError_t e = fa::launch_bwd(a, d, dtype == FA_BF16, band, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

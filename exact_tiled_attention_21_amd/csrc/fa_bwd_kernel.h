@@ -1,6 +1,7 @@
 // Exact attention backward pass on gfx950 (MFMA 32x32x16).
 //
-// For O = softmax(scale Q K^T) V (with the causal mask, if any) and an upstream
+// For O = softmax(scale Q K^T) V (with a causal mask or sliding-window band, if
+// any) and an upstream
 // gradient dO, with P the softmax probabilities and D_i = sum_c dO[i][c] O[i][c]:
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
 // As in the forward pass no score matrix is stored: P is recomputed tile by tile
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const BwdArgs a) {
 
 // ---------------------------------------------------------------- dK, dV
 
-template <int D, bool BF16, bool CAUSAL> struct DkdvWave {
+template <int D, bool BF16, bool BAND> struct DkdvWave {
   using C = BwdCfg<D>;
   using E = Elem<BF16>;
   using T = typename E::T;
@@ -146,7 +147,8 @@ template <int D, bool BF16, bool CAUSAL> struct DkdvWave {
   const BwdArgs& a;
   int lane, wave, hh;
   int b, g, key, k0w, diag;
-  int nqt, t0, nqp;
+  int nqt, t0, t1, nqp;   // query tiles [t0, t1) see some key of the workgroup
+  int qlo, qspan;         // rows q that see this lane's key: 0 <= q - qlo <= qspan (unsigned)
   uint32_t qpitch;
   V8 kf[C::NS], vf[C::NS];          // this lane's key row of K and V (B operands)
   f32x16 dvt[C::NCB], dkt[C::NCB];  // dV^T and dK^T, [d][key]
@@ -161,8 +163,16 @@ template <int D, bool BF16, bool CAUSAL> struct DkdvWave {
     diag = a.Nk - a.Nq;
     nqt = (a.Nq + C::BQ - 1) / C::BQ;
     nqp = bwd_nq_pad(a.Nq);
-    // causal: query tiles before the first row that sees key k0 contribute nothing
-    t0 = CAUSAL ? min(nqt, max(0, k0 - diag) / C::BQ) : 0;
+    // band: row q sees key j iff q + diag - wl <= j <= q + diag + wr (a side
+    // at -1 is open; causal is (-1, 0)), so key j is seen by rows
+    // j - diag - wr .. j - diag + wl
+    const bool has_l = BAND && a.wl >= 0, has_r = BAND && a.wr >= 0;
+    qlo = has_r ? key - diag - a.wr : -(1 << 29);
+    qspan = (has_l ? key - diag + a.wl : (1 << 29)) - qlo;
+    const int qa = has_r ? max(0, k0 - diag - a.wr) : 0;
+    const int qb = has_l ? min(a.Nq - 1, k0 + C::WROWS - 1 - diag + a.wl) : a.Nq - 1;
+    t0 = min(nqt, qa / C::BQ);
+    t1 = qb >= qa ? min(nqt, qb / C::BQ + 1) : t0;
     qpitch = static_cast<uint32_t>(a.Hq) * D * 2;
     const size_t kv = ((static_cast<size_t>(b) * a.Nk + key) * a.Hkv + g) * D + 8 * hh;
     const T* kp = reinterpret_cast<const T*>(a.k) + kv;
@@ -213,7 +223,7 @@ template <int D, bool BF16, bool CAUSAL> struct DkdvWave {
       float pr = exp2_fast(__builtin_fmaf(s[r], a.sl2, -l4[r >> 2][r & 3]));
       if (MASK) {
         const int q = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        pr = (key > q + diag) ? 0.f : pr;
+        pr = (static_cast<uint32_t>(q - qlo) > static_cast<uint32_t>(qspan)) ? 0.f : pr;
       }
       p[r] = pr;
       ds[r] = pr * (dp[r] - d4[r >> 2][r & 3]);
@@ -283,7 +293,7 @@ template <int D, bool BF16, bool CAUSAL> struct DkdvWave {
   __device__ __forceinline__ void step(int hi, int t, const BwdLds& lds) {
     {
       int hn = hi, tn = t + 1;
-      if (tn == nqt) {
+      if (tn == t1) {
         hn = hi + 1;
         tn = t0;
       }
@@ -351,7 +361,7 @@ template <int D, bool BF16, bool CAUSAL> struct DkdvWave {
   }
 };
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool BAND>
 __global__ __launch_bounds__(BwdCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fa_bwd_dkdv_kernel(const BwdArgs a) {
   using C = BwdCfg<D>;
@@ -364,8 +374,8 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
 
   const int nkt = (a.Nk + C::WROWS - 1) / C::WROWS;
   int kt, gb;
-  if (CAUSAL) {
-    // the first key tiles see the most query rows
+  if (BAND) {
+    // with a causal band the first key tiles see the most query rows
     blocked_order(blockIdx.x, nkt, a.Hkv * a.B, a.hb_kv, kt, gb);
   } else {
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -375,29 +385,32 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
   const int g = gb % a.Hkv;
   const int b = gb / a.Hkv;
   const int k0 = kt * C::WROWS;
-  DkdvWave<D, BF16, CAUSAL> w(a, b, g, k0);
+  DkdvWave<D, BF16, BAND> w(a, b, g, k0);
   const BwdLds lds{{q_lds0, q_lds1}, {o_lds0, o_lds1}, {st_lds0, st_lds1}};
 
-  // causal: tiles [t0, tm) hold rows for which some key of the workgroup is
-  // masked (the diagonal); later tiles see every key of it
-  int tm = w.t0;
-  if (CAUSAL) {
-    const int x = k0 + C::WROWS - w.diag;   // first row that sees every key
-    tm = min(w.nqt, max(w.t0, x > 0 ? (x + C::BQ - 1) / C::BQ : 0));
+  // tiles [u0, u1) hold only rows that see every key of the workgroup; the
+  // tiles before and after them (the band's edges) are computed with the mask
+  int u0 = w.t0, u1 = w.t1;
+  if (BAND) {
+    const int ua = a.wr >= 0 ? k0 + C::WROWS - 1 - w.diag - a.wr : 0;   // first row seeing all keys
+    const int ub = a.wl >= 0 ? k0 - w.diag + a.wl : (1 << 30);            // last such row
+    u0 = min(w.t1, max(w.t0, ua > 0 ? (ua + C::BQ - 1) / C::BQ : 0));
+    u1 = max(u0, min(w.t1, ub >= 0 ? (ub + 1) / C::BQ : 0));
   }
-  if (w.t0 < w.nqt) w.fetch(0, w.t0, lds.x[0], lds.y[0], lds.st[0]);
+  if (w.t0 < w.t1) w.fetch(0, w.t0, lds.x[0], lds.y[0], lds.st[0]);
   __syncthreads();
   int n = 0;
-  for (int hi = 0; hi < a.group && w.t0 < w.nqt; ++hi) {
-    w.template run<true>(hi, w.t0, tm, n, lds);
-    w.template run<false>(hi, tm, w.nqt, n, lds);
+  for (int hi = 0; hi < a.group && w.t0 < w.t1; ++hi) {
+    w.template run<true>(hi, w.t0, u0, n, lds);
+    w.template run<false>(hi, u0, u1, n, lds);
+    w.template run<true>(hi, u1, w.t1, n, lds);
   }
   w.finish();
 }
 
 // ---------------------------------------------------------------- dQ
 
-template <int D, bool BF16, bool CAUSAL> struct DqWave {
+template <int D, bool BF16, bool BAND> struct DqWave {
   using C = BwdCfg<D>;
   using E = Elem<BF16>;
   using T = typename E::T;
@@ -406,6 +419,8 @@ template <int D, bool BF16, bool CAUSAL> struct DqWave {
   const BwdArgs& a;
   int lane, wave, hh;
   int b, hq, qrow, diag;
+  int klo, kspan;            // keys k this lane's row sees: 0 <= k - klo <= kspan (unsigned), k < Nk
+  int j0;                    // first key tile of the workgroup (its LDS stage 0)
   float lse2, dsum;
   const char* kg;
   const char* vg;
@@ -423,6 +438,10 @@ template <int D, bool BF16, bool CAUSAL> struct DqWave {
     qrow = q0 + wave * C::BT + (lane & 31);
     diag = a.Nk - a.Nq;
     nsteps = 0;
+    j0 = 0;
+    const bool has_l = BAND && a.wl >= 0, has_r = BAND && a.wr >= 0;
+    klo = has_l ? qrow + diag - a.wl : -(1 << 29);
+    kspan = (has_r ? qrow + diag + a.wr : (1 << 29)) - klo;
     const bool live = qrow < a.Nq;
     const size_t r = ((static_cast<size_t>(b) * a.Nq + qrow) * a.Hq + hq) * D + 8 * hh;
     const T* qp = reinterpret_cast<const T*>(a.q) + r;
@@ -488,7 +507,7 @@ template <int D, bool BF16, bool CAUSAL> struct DqWave {
       float pr = exp2_fast(__builtin_fmaf(s[r], a.sl2, -lse2));
       if (MASK) {
         const int kk = j * C::BT + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const bool hide = CAUSAL ? (kk >= a.Nk || kk > qrow + diag) : (kk >= a.Nk);
+        const bool hide = kk >= a.Nk || (BAND && static_cast<uint32_t>(kk - klo) > static_cast<uint32_t>(kspan));
         pr = hide ? 0.f : pr;
       }
       ds[r] = pr * (dp[r] - dsum);
@@ -513,10 +532,10 @@ template <int D, bool BF16, bool CAUSAL> struct DqWave {
     __syncthreads();
   }
 
-  // key tiles [j, je), tile j in stage j & 1
+  // key tiles [j, je), tile j in stage (j - j0) & 1
   template <bool MASK>
   __device__ __forceinline__ void run(int j, int je, const BwdLds& lds) {
-    if (j < je && (j & 1)) {
+    if (j < je && ((j - j0) & 1)) {
       step<1, MASK>(j, lds);
       ++j;
     }
@@ -543,7 +562,7 @@ template <int D, bool BF16, bool CAUSAL> struct DqWave {
   }
 };
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool BAND>
 __global__ __launch_bounds__(BwdCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1, D <= 128 ? 2 : 1)))
 void fa_bwd_dq_kernel(const BwdArgs a) {
   using C = BwdCfg<D>;
@@ -554,8 +573,8 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
 
   const int nqt = (a.Nq + C::WROWS - 1) / C::WROWS;
   int qt, hb;
-  if (CAUSAL) {
-    // the last query tiles see the most keys
+  if (BAND) {
+    // with a causal band the last query tiles see the most keys
     int o;
     blocked_order(blockIdx.x, nqt, a.Hq * a.B, a.hb_q, o, hb);
     qt = nqt - 1 - o;
@@ -567,27 +586,32 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
   const int hq = hb % a.Hq;
   const int b = hb / a.Hq;
   const int q0 = qt * C::WROWS;
-  DqWave<D, BF16, CAUSAL> w(a, b, hq, q0);
+  DqWave<D, BF16, BAND> w(a, b, hq, q0);
   const BwdLds lds{{k_lds0, k_lds1}, {v_lds0, v_lds1}, {nullptr, nullptr}};
 
-  // key tiles the workgroup needs (causal: up to its last row's diagonal), and
-  // the first one where some row needs an element mask (key tail, diagonal)
+  // key tiles [j0, nsteps) hold a key some row of the workgroup sees; tiles
+  // [u0, u1) hold only keys every row sees (below Nk); the others are masked
   const int last = min(q0 + C::WROWS, a.Nq) - 1;
-  const int kend = CAUSAL ? min(a.Nk, last + w.diag + 1) : a.Nk;
-  w.nsteps = kend > 0 ? (kend + C::BT - 1) / C::BT : 0;
-  int jm = a.Nk / C::BT;
-  if (CAUSAL) jm = min(jm, max(0, q0 + w.diag + 1) / C::BT);
-  jm = min(jm, w.nsteps);
+  const bool has_l = BAND && a.wl >= 0, has_r = BAND && a.wr >= 0;
+  const int ka = has_l ? max(0, q0 + w.diag - a.wl) : 0;
+  const int kb = has_r ? min(a.Nk - 1, last + w.diag + a.wr) : a.Nk - 1;
+  w.j0 = ka / C::BT;
+  w.nsteps = kb >= ka ? kb / C::BT + 1 : w.j0;
+  const int ua = has_l ? max(0, last + w.diag - a.wl) : 0;
+  const int ub = min(a.Nk - 1, has_r ? q0 + w.diag + a.wr : a.Nk - 1);
+  const int u0 = min(w.nsteps, max(w.j0, (ua + C::BT - 1) / C::BT));
+  const int u1 = max(u0, min(w.nsteps, ub >= 0 ? (ub + 1) / C::BT : 0));
 
-  if (w.nsteps > 0) w.fetch(0, lds.x[0], lds.y[0]);
+  if (w.nsteps > w.j0) w.fetch(w.j0, lds.x[0], lds.y[0]);
   __syncthreads();
-  w.template run<false>(0, jm, lds);
-  w.template run<true>(jm, w.nsteps, lds);
+  w.template run<true>(w.j0, u0, lds);
+  w.template run<false>(u0, u1, lds);
+  w.template run<true>(u1, w.nsteps, lds);
   w.finish();
 }
 
 template <int D>
-hipError_t launch_bwd_d(const BwdArgs& a, bool bf16, bool causal, hipStream_t stream) {
+hipError_t launch_bwd_d(const BwdArgs& a, bool bf16, bool band, hipStream_t stream) {
   using C = BwdCfg<D>;
   (void)hipGetLastError();   // start from a clean error state
   {
@@ -602,7 +626,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, bool bf16, bool causal, hipStream_t st
   const dim3 grid_kv(static_cast<unsigned>((a.Nk + C::WROWS - 1) / C::WROWS) * a.Hkv * a.B);
   const dim3 grid_q(static_cast<unsigned>((a.Nq + C::WROWS - 1) / C::WROWS) * a.Hq * a.B);
   if (bf16) {
-    if (causal) {
+    if (band) {
       fa_bwd_dkdv_kernel<D, true, true><<<grid_kv, block, 0, stream>>>(a);
       fa_bwd_dq_kernel<D, true, true><<<grid_q, block, 0, stream>>>(a);
     } else {
@@ -610,7 +634,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, bool bf16, bool causal, hipStream_t st
       fa_bwd_dq_kernel<D, true, false><<<grid_q, block, 0, stream>>>(a);
     }
   } else {
-    if (causal) {
+    if (band) {
       fa_bwd_dkdv_kernel<D, false, true><<<grid_kv, block, 0, stream>>>(a);
       fa_bwd_dq_kernel<D, false, true><<<grid_q, block, 0, stream>>>(a);
     } else {

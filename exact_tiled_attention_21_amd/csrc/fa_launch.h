@@ -67,6 +67,9 @@ struct BwdArgs {
   int group;         // Hq / Hkv
   float sl2;         // scale * log2(e)
   float scale;
+  // band of visible keys for query i (diag = Nk - Nq): i + diag - wl <= j <= i + diag + wr;
+  // -1 leaves that side open. Causal is wl = -1, wr = 0.
+  int wl, wr;
   int hb_kv, hb_q;   // heads per block of the heaviest-first causal orders (dK/dV, dQ)
 };
 
@@ -85,6 +88,7 @@ constexpr int fwd_rows(int) { return 128; }
 // band: apply the (wl, wr) band (causal or a sliding window)
 hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool band, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool causal, hipStream_t stream);
+// band: apply the (wl, wr) band (causal or a sliding window)
+hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool band, hipStream_t stream);
 
 }  // namespace fa

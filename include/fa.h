@@ -230,6 +230,18 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int Hkv, int d, int causal, float scale, fa_dtype dtype, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/*
+ * Attention backward pass with a sliding window: the gradients of
+ * fa_fwd_window's result, with the band, its bottom-right alignment, the -1
+ * convention and causal fixing window_right = 0 as there. fa_bwd is this call
+ * with window (-1, -1). Other arguments, layouts and status codes as in
+ * fa_bwd; FA_ERR_SHAPE for a window side below -1.
+ */
+fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, int B, int Nq, int Nk, int Hq,
+                        int Hkv, int d, int window_left, int window_right, int causal, float scale,
+                        fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_str(fa_status status);
 

@@ -178,3 +178,11 @@ def bwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE
 ])
 def test_bwd_rejects_invalid_arguments(lib, kw, status):
     assert bwd(lib, **kw) == status
+
+
+@pytest.mark.parametrize("wl,wr,status", [(-2, 0, 2), (0, -2, 2), (-1, -1, 1)])
+def test_bwd_window_rejects_invalid_windows(lib, wl, wr, status):
+    q = None if status == 1 else FAKE   # a valid window reaches the pointer check
+    wsb = lib.fa_bwd_workspace_bytes(1, 8, 2)
+    assert lib.fa_bwd_window(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8, 2, 1, 64, wl, wr, 0,
+                             0.125, 1, FAKE, wsb, None) == status

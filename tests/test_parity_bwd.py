@@ -34,23 +34,24 @@ def inputs(wid, B, Nq, Nk, Hq, Hkv, d, dtype):
     return qb, kb, vb, dob
 
 
-def run_full(wid, B, Nq, Nk, Hq, Hkv, d, dtype, causal, scale=None, fwd="gpu"):
+def run_full(wid, B, Nq, Nk, Hq, Hkv, d, dtype, causal, scale=None, fwd="gpu", window=(-1, -1)):
     qb, kb, vb, dob = inputs(wid, B, Nq, Nk, Hq, Hkv, d, dtype)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    what = f"wid={wid} B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} {dtype} causal={causal} fwd={fwd}"
+    what = (f"wid={wid} B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} {dtype} causal={causal} fwd={fwd} "
+            f"window={window}")
     print(f"[bwd] {what}", flush=True)
     q, k, v, do = (oracle.widen(x, dtype) for x in (qb, kb, vb, dob))
     qd, kd, vd, dod = (to_dev(x, dtype) for x in (qb, kb, vb, dob))
     if fwd == "gpu":
-        o, lse = attention(qd, kd, vd, causal=causal, scale=scale)
+        o, lse = attention(qd, kd, vd, causal=causal, scale=scale, window=window)
     else:
         import torch
-        o_ref, lse_ref = oracle.attention(q, k, v, causal=causal, scale=scale)
+        o_ref, lse_ref = oracle.attention(q, k, v, causal=causal, scale=scale, window=window)
         o = to_dev(synthetic.to_bits(o_ref.astype(np.float32), dtype), dtype)
         lse = torch.from_numpy(lse_ref.astype(np.float32)).to(qd.device)
-    dq, dk, dv = attention_backward(qd, kd, vd, o, lse, dod, causal=causal, scale=scale)
-    ref = oracle.backward(q, k, v, do, causal=causal, scale=scale)
-    mag = oracle.backward_magnitudes(q, k, v, do, causal=causal, scale=scale)
+    dq, dk, dv = attention_backward(qd, kd, vd, o, lse, dod, causal=causal, scale=scale, window=window)
+    ref = oracle.backward(q, k, v, do, causal=causal, scale=scale, window=window)
+    mag = oracle.backward_magnitudes(q, k, v, do, causal=causal, scale=scale, window=window)
     worst = [cmp.check_grad(to_np(g), r, m, dtype, f"{what} {n}")
              for g, r, m, n in zip((dq, dk, dv), ref, mag, ("dq", "dk", "dv"))]
     print(f"[bwd] ratio to u*M: dq {worst[0]:.3g} dk {worst[1]:.3g} dv {worst[2]:.3g}", flush=True)
@@ -125,6 +126,46 @@ def test_autograd_function():
     assert torch.equal(out.view(torch.int16), o.view(torch.int16))
     for leaf, g in zip(leaves, direct):
         assert torch.equal(leaf.grad.view(torch.int16), g.view(torch.int16))
+
+
+WINDOWS = [(0, 0), (16, 0), (100, 100), (-1, 50), (300, -1), (0, -1), (63, 64), (1000, 1000), (-1, 0)]
+
+
+@pytest.mark.parametrize("window", WINDOWS, ids=lambda w: f"{w[0]}_{w[1]}")
+def test_window(window):
+    # several key and query tiles on both sides of the band, ragged tails
+    run_full(700 + WINDOWS.index(window), 2, 333, 333, 4, 2, 128, "bf16", False, window=window)
+
+
+@pytest.mark.parametrize("case", [(200, 450, False), (450, 200, False), (300, 300, True)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_window_alignment_and_causal(case):
+    # bottom-right alignment with Nq != Nk both ways (rows or keys outside every band),
+    # and causal fixing the right edge of a (left, right) window at 0
+    Nq, Nk, causal = case
+    run_full(720 + Nq % 97, 1, Nq, Nk, 4, 1, 64, "f16", causal, window=(40, 25))
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_window_head_dims(d):
+    run_full(730 + HEAD_DIMS.index(d), 1, 260, 260, 2, 1, d, "bf16", False, window=(70, 10))
+
+
+def test_window_oracle_forward_inputs():
+    run_full(740, 1, 300, 300, 2, 2, 128, "bf16", False, fwd="oracle", window=(50, 50))
+
+
+def test_window_open_band_equals_plain():
+    """(-1, -1) through attention_backward takes fa_bwd; a band wider than the
+    sequence through fa_bwd_window must give the same bits."""
+    import torch
+    qb, kb, vb, dob = inputs(741, 1, 300, 300, 4, 2, 128, "bf16")
+    qd, kd, vd, dod = (to_dev(x, "bf16") for x in (qb, kb, vb, dob))
+    o, lse = attention(qd, kd, vd)
+    plain = attention_backward(qd, kd, vd, o, lse, dod)
+    wide = attention_backward(qd, kd, vd, o, lse, dod, window=(100000, 100000))
+    for a, b in zip(plain, wide):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 @pytest.mark.parametrize("name", ["bwd_bf16_4096_full", "bwd_bf16_4096_causal"])
