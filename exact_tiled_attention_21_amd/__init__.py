@@ -11,6 +11,8 @@ kernels of libfa.so. torch supplies device memory and the current stream.
                scale=None, causal=False) -> (o, lse)
   attention_backward(q, k, v, o, lse, dout, causal=False, scale=None,
                      window=(-1, -1)) -> (dq, dk, dv)
+  attention_varlen_backward(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k,
+                            max_seqlen_q, max_seqlen_k, causal=False, scale=None) -> (dq, dk, dv)
   attention_func(q, k, v, causal=False, scale=None, window=(-1, -1)) -> o, differentiable
 
 Tensors are [batch, seq_len, heads, head_dim], fp16 or bf16, contiguous, on a
@@ -24,7 +26,8 @@ import math
 
 from ._lib import FA_BF16, FA_F16, FA_MAX_SPLITS, FaError, load, status_str  # noqa: F401
 
-__all__ = ["attention", "attention_varlen", "attention_backward", "attention_func", "bwd_workspace_bytes", "decode",
+__all__ = ["attention", "attention_varlen", "attention_backward", "attention_varlen_backward", "attention_func",
+           "bwd_workspace_bytes", "decode",
            "decode_paged", "decode_workspace_bytes", "FaError", "load"]
 
 
@@ -238,6 +241,52 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
                                       workspace.numel() * workspace.element_size(), _stream(q))
     if st != 0:
         raise FaError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def attention_varlen_backward(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                              max_seqlen_k: int, causal: bool = False, scale: float | None = None,
+                              workspace=None, dq=None, dk=None, dv=None):
+    """Gradients of attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, ...) for dout.
+
+    q, o, dout [total_q, Hq, d]; k, v [total_k, Hkv, d]; lse float32 [Hq, total_q] as
+    attention_varlen returns it; max_seqlen_q/k at least every sequence's length."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not t.is_cuda or t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [tokens, heads, head_dim] device tensor")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype):
+        raise TypeError("q, k, v, o, dout must share a dtype")
+    if k.shape != v.shape or q.shape[2] != k.shape[2] or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("k and v must match; o and dout must match q; head_dim must agree")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if not t.is_cuda or t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device vector")
+    if cu_seqlens_q.shape != cu_seqlens_k.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have B + 1 entries")
+    total_q, Hq, d = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.shape[0] - 1
+    if (not lse.is_cuda or lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, total_q)
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 device tensor [Hq, total_q]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = bwd_workspace_bytes(B, int(max_seqlen_q), Hq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    with torch.cuda.device(q.device):
+        st = load().fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                  cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, int(max_seqlen_q),
+                                  int(max_seqlen_k), total_q, total_k, Hq, Hkv, d, int(bool(causal)),
+                                  float(scale), _dtype_code(q), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_bwd_varlen")
     return dq, dk, dv
 
 

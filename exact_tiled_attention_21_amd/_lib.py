@@ -12,7 +12,8 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_NULLPTR", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADS",
           5: "FA_ERR_DTYPE", 6: "FA_ERR_SPLITS", 7: "FA_ERR_WORKSPACE", 8: "FA_ERR_LAUNCH",
           9: "FA_ERR_ALIGN", 10: "FA_ERR_SCALE"}
 EXPORTS = ("fa_fwd", "fa_fwd_window", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_splitkv",
-           "fa_decode_splitkv_paged", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_window", "fa_status_str")
+           "fa_decode_splitkv_paged", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_window", "fa_bwd_varlen",
+           "fa_status_str")
 
 _lib = None
 
@@ -51,6 +52,8 @@ def load(path: str = LIB_PATH):
     lib.fa_bwd.restype = I
     lib.fa_bwd_window.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P, S, P]
     lib.fa_bwd_window.restype = I
+    lib.fa_bwd_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P, S, P]
+    lib.fa_bwd_varlen.restype = I
     lib.fa_status_str.argtypes = [I]
     lib.fa_status_str.restype = ctypes.c_char_p
     if path == LIB_PATH:

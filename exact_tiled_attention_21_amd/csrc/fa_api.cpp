@@ -143,6 +143,40 @@ fa_status fwd_common(fa::FwdArgs& a, int d, int wl, int wr, int causal, float sc
 // rows of each backward statistics array: [B][Hq][Nq rounded up to 64]
 size_t bwd_stat_rows(int B, int Nq, int Hq) { return size_t(B) * Hq * ((size_t(Nq) + 63) / 64 * 64); }
 
+fa_status bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, const int* cu_q, const int* cu_k,
+                     int total_q, int total_k, int B, int Nq, int Nk, int Hq, int Hkv, int d,
+                     int window_left, int window_right, int causal, float scale, fa_dtype dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_NULLPTR;
+  if (window_left < -1 || window_right < -1) return FA_ERR_SHAPE;
+  if (workspace_bytes < fa_bwd_workspace_bytes(B, Nq, Hq)) return FA_ERR_WORKSPACE;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return FA_ERR_ALIGN;
+  const int64_t nkt = (int64_t(Nk) + 127) / 128, nqt = (int64_t(Nq) + 127) / 128;
+  if (nkt * Hkv * B > 0x7fffffffLL || nqt * Hq * B > 0x7fffffffLL) return FA_ERR_SHAPE;
+  // both statistics arrays addressed with 32-bit byte offsets
+  if (bwd_stat_rows(B, Nq, Hq) > 0x0fffffffu) return FA_ERR_SHAPE;
+  fa::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  const size_t rows = bwd_stat_rows(B, Nq, Hq);
+  a.dsum = static_cast<float*>(workspace);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + pad256(rows * sizeof(float)));
+  a.B = B; a.Nq = Nq; a.Nk = Nk; a.Hq = Hq; a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  a.sl2 = scale * 1.4426950408889634f;
+  a.scale = scale;
+  a.cu_q = cu_q; a.cu_k = cu_k; a.total_q = total_q; a.total_k = total_k;
+  a.wl = window_left;
+  a.wr = causal ? 0 : window_right;
+  a.hb_kv = fa::order_block_heads(int64_t(Hkv) * B, int64_t(a.group) * Nq * d * 4);   // Q and dO of a group
+  a.hb_q = fa::order_block_heads(int64_t(Hq) * B, int64_t(Nk) * d * 4 / a.group);     // K and V per query head
+  const bool band = a.wl >= 0 || a.wr >= 0;
+  hipError_t e = fa::launch_bwd(a, d, dtype == FA_BF16, band, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -263,33 +297,28 @@ fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void*
                         fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
   fa_status st = check_common(q, k, v, const_cast<void*>(o), lse, B, Nq, Nk, Hq, Hkv, d, scale, dtype);
   if (st != FA_OK) return st;
-  if (!lse || !dout || !dq || !dk || !dv || !workspace) return FA_ERR_NULLPTR;
-  if (window_left < -1 || window_right < -1) return FA_ERR_SHAPE;
-  if (workspace_bytes < fa_bwd_workspace_bytes(B, Nq, Hq)) return FA_ERR_WORKSPACE;
-  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
-    return FA_ERR_ALIGN;
-  const int64_t nkt = (int64_t(Nk) + 127) / 128, nqt = (int64_t(Nq) + 127) / 128;
-  if (nkt * Hkv * B > 0x7fffffffLL || nqt * Hq * B > 0x7fffffffLL) return FA_ERR_SHAPE;
-  // both statistics arrays addressed with 32-bit byte offsets
-  if (bwd_stat_rows(B, Nq, Hq) > 0x0fffffffu) return FA_ERR_SHAPE;
-  fa::BwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
-  a.dq = dq; a.dk = dk; a.dv = dv;
-  const size_t rows = bwd_stat_rows(B, Nq, Hq);
-  a.dsum = static_cast<float*>(workspace);
-  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + pad256(rows * sizeof(float)));
-  a.B = B; a.Nq = Nq; a.Nk = Nk; a.Hq = Hq; a.Hkv = Hkv;
-  a.group = Hq / Hkv;
-  a.sl2 = scale * 1.4426950408889634f;
-  a.scale = scale;
-  a.wl = window_left;
-  a.wr = causal ? 0 : window_right;
-  a.hb_kv = fa::order_block_heads(int64_t(Hkv) * B, int64_t(a.group) * Nq * d * 4);   // Q and dO of a group
-  a.hb_q = fa::order_block_heads(int64_t(Hq) * B, int64_t(Nk) * d * 4 / a.group);     // K and V per query head
-  const bool band = a.wl >= 0 || a.wr >= 0;
-  hipError_t e = fa::launch_bwd(a, d, dtype == FA_BF16, band, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, nullptr, nullptr, 0, 0, B, Nq, Nk, Hq, Hkv, d,
+                    window_left, window_right, causal, scale, dtype, workspace, workspace_bytes, stream);
 }
+
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
+                        const int* cu_seqlens_k, int B, int max_seqlen_q, int max_seqlen_k, int total_q,
+                        int total_k, int Hq, int Hkv, int d, int causal, float scale, fa_dtype dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULLPTR;
+  // the common checks, with the packed tensors as one batch element of total rows
+  fa_status st = check_common(q, k, v, const_cast<void*>(o), lse, 1, total_q, total_k, Hq, Hkv, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (B < 1 || max_seqlen_q < 1 || max_seqlen_k < 1) return FA_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return FA_ERR_ALIGN;
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, total_q, total_k, B,
+                    max_seqlen_q, max_seqlen_k, Hq, Hkv, d, -1, -1, causal, scale, dtype, workspace,
+                    workspace_bytes, stream);
+}
+
+
 
 const char* fa_status_str(fa_status s) {
   switch (s) {

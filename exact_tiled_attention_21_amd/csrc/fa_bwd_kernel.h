@@ -94,6 +94,38 @@ __device__ __forceinline__ V8 row_frag(const char* t, int s, int lane) {
 // Padded row count of the per-row statistics (whole dK/dV query tiles).
 __host__ __device__ constexpr int bwd_nq_pad(int nq) { return (nq + 63) / 64 * 64; }
 
+// The sequence of batch element b: its query and key counts and the first rows
+// of its Q/dO/dQ and K/V/dK/dV in the (padded or packed) tensors, and the
+// first entry of its LSE rows. A packed batch reads its bounds from the prefix
+// sums, clamped into the tensors so that a malformed table cannot lead outside
+// them. The row statistics are always [B][Hq][max rows rounded up to 64].
+struct BwdSeq {
+  int nq, nk;
+  size_t q_row0, k_row0;
+  __device__ __forceinline__ BwdSeq(const BwdArgs& a, int b) {
+    if (a.cu_q != nullptr) {
+      const int q_lo = min(max(a.cu_q[b], 0), a.total_q);
+      const int q_hi = min(max(a.cu_q[b + 1], q_lo), a.total_q);
+      const int k_lo = min(max(a.cu_k[b], 0), a.total_k);
+      const int k_hi = min(max(a.cu_k[b + 1], k_lo), a.total_k);
+      nq = min(q_hi - q_lo, a.Nq);
+      nk = min(k_hi - k_lo, a.Nk);
+      q_row0 = q_lo;
+      k_row0 = k_lo;
+    } else {
+      nq = a.Nq;
+      nk = a.Nk;
+      q_row0 = static_cast<size_t>(b) * a.Nq;
+      k_row0 = static_cast<size_t>(b) * a.Nk;
+    }
+  }
+  // LSE of query head h, row i: [B][Hq][Nq], or [Hq][total_q] for a packed batch
+  __device__ __forceinline__ size_t lse_index(const BwdArgs& a, int b, int h, int i) const {
+    return a.cu_q != nullptr ? static_cast<size_t>(h) * a.total_q + q_row0 + i
+                             : (static_cast<size_t>(b) * a.Hq + h) * a.Nq + i;
+  }
+};
+
 // ---------------------------------------------------------------- preprocess
 
 // G lanes per statistics entry (b, h, i), i < Nq rounded up to 64:
@@ -113,11 +145,12 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const BwdArgs a) {
   const int i = static_cast<int>(e % nqp);
   const int64_t bh = e / nqp;
   const int h = static_cast<int>(bh % a.Hq);
-  const int64_t b = bh / a.Hq;
-  const bool live = e < entries && i < a.Nq;
+  const int b = static_cast<int>(bh / a.Hq);
+  const BwdSeq sq(a, e < entries ? b : 0);
+  const bool live = e < entries && i < sq.nq;
   float acc = 0.f;
   if (live && c < CPR) {
-    const int64_t row = ((b * a.Nq + i) * a.Hq + h) * D + 8 * c;
+    const int64_t row = ((static_cast<int64_t>(sq.q_row0) + i) * a.Hq + h) * D + 8 * c;
     const T8 o8 = *reinterpret_cast<const T8*>(reinterpret_cast<const T*>(a.o) + row);
     const T8 d8 = *reinterpret_cast<const T8*>(reinterpret_cast<const T*>(a.dout) + row);
 #pragma unroll
@@ -128,7 +161,7 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const BwdArgs a) {
   if (e < entries && c == 0) {
     float l2 = __builtin_huge_valf();
     if (live) {
-      const float l = a.lse[bh * a.Nq + i];
+      const float l = a.lse[sq.lse_index(a, b, h, i)];
       if (l != kNegInf) l2 = l * kLog2e;
     }
     a.dsum[e] = live ? acc : 0.f;
@@ -145,6 +178,7 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
   using V8 = typename E::V8;
 
   const BwdArgs& a;
+  const BwdSeq& sq;
   int lane, wave, hh;
   int b, g, key, k0w, diag;
   int nqt, t0, t1, nqp;   // query tiles [t0, t1) see some key of the workgroup
@@ -154,14 +188,15 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
   f32x16 dvt[C::NCB], dkt[C::NCB];  // dV^T and dK^T, [d][key]
   BwdDma<D, C::BQ> dma;
 
-  __device__ __forceinline__ DkdvWave(const BwdArgs& args, int b_, int g_, int k0) : a(args), b(b_), g(g_) {
+  __device__ __forceinline__ DkdvWave(const BwdArgs& args, const BwdSeq& seq, int b_, int g_, int k0)
+      : a(args), sq(seq), b(b_), g(g_) {
     lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     hh = lane >> 5;
     k0w = k0 + wave * C::BT;
     key = k0w + (lane & 31);
-    diag = a.Nk - a.Nq;
-    nqt = (a.Nq + C::BQ - 1) / C::BQ;
+    diag = sq.nk - sq.nq;
+    nqt = (sq.nq + C::BQ - 1) / C::BQ;
     nqp = bwd_nq_pad(a.Nq);
     // band: row q sees key j iff q + diag - wl <= j <= q + diag + wr (a side
     // at -1 is open; causal is (-1, 0)), so key j is seen by rows
@@ -170,17 +205,17 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
     qlo = has_r ? key - diag - a.wr : -(1 << 29);
     qspan = (has_l ? key - diag + a.wl : (1 << 29)) - qlo;
     const int qa = has_r ? max(0, k0 - diag - a.wr) : 0;
-    const int qb = has_l ? min(a.Nq - 1, k0 + C::WROWS - 1 - diag + a.wl) : a.Nq - 1;
+    const int qb = has_l ? min(sq.nq - 1, k0 + C::WROWS - 1 - diag + a.wl) : sq.nq - 1;
     t0 = min(nqt, qa / C::BQ);
     t1 = qb >= qa ? min(nqt, qb / C::BQ + 1) : t0;
     qpitch = static_cast<uint32_t>(a.Hq) * D * 2;
-    const size_t kv = ((static_cast<size_t>(b) * a.Nk + key) * a.Hkv + g) * D + 8 * hh;
+    const size_t kv = ((sq.k_row0 + key) * a.Hkv + g) * D + 8 * hh;
     const T* kp = reinterpret_cast<const T*>(a.k) + kv;
     const T* vp = reinterpret_cast<const T*>(a.v) + kv;
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) {
-      kf[s] = key < a.Nk ? *reinterpret_cast<const V8*>(kp + 16 * s) : V8{};
-      vf[s] = key < a.Nk ? *reinterpret_cast<const V8*>(vp + 16 * s) : V8{};
+      kf[s] = key < sq.nk ? *reinterpret_cast<const V8*>(kp + 16 * s) : V8{};
+      vf[s] = key < sq.nk ? *reinterpret_cast<const V8*>(vp + 16 * s) : V8{};
     }
 #pragma unroll
     for (int cb = 0; cb < C::NCB; ++cb) {
@@ -194,8 +229,8 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
   // their statistics: the log2 LSE of the 64 rows, then their D (lanes 0..15
   // and 16..31 of wave 0 move 16 bytes each)
   __device__ __forceinline__ void fetch(int hi, int t, char* ql, char* ol, float* stl) const {
-    const size_t off = ((static_cast<size_t>(b) * a.Nq + t * C::BQ) * a.Hq + g * a.group + hi) * D * 2;
-    const int64_t valid = static_cast<int64_t>(a.Nq - t * C::BQ - 1) * qpitch + D * 2;
+    const size_t off = ((sq.q_row0 + t * C::BQ) * a.Hq + g * a.group + hi) * D * 2;
+    const int64_t valid = static_cast<int64_t>(sq.nq - t * C::BQ - 1) * qpitch + D * 2;
     dma.issue(reinterpret_cast<const char*>(a.q) + off, valid, ql);
     dma.issue(reinterpret_cast<const char*>(a.dout) + off, valid, ol);
     if (wave == 0 && lane < 32) {
@@ -340,8 +375,8 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
 
   // dV, and dK = scale (dK^T)^T, rounded to the element type
   __device__ __forceinline__ void finish() const {
-    if (key >= a.Nk) return;
-    const size_t row = ((static_cast<size_t>(b) * a.Nk + key) * a.Hkv + g) * D;
+    if (key >= sq.nk) return;
+    const size_t row = ((sq.k_row0 + key) * a.Hkv + g) * D;
     T* dvp = reinterpret_cast<T*>(a.dv) + row;
     T* dkp = reinterpret_cast<T*>(a.dk) + row;
     typedef T T4 __attribute__((ext_vector_type(4)));
@@ -385,7 +420,9 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
   const int g = gb % a.Hkv;
   const int b = gb / a.Hkv;
   const int k0 = kt * C::WROWS;
-  DkdvWave<D, BF16, BAND> w(a, b, g, k0);
+  const BwdSeq sq(a, b);
+  if (k0 >= sq.nk) return;   // a packed sequence shorter than the grid: uniform, before any barrier
+  DkdvWave<D, BF16, BAND> w(a, sq, b, g, k0);
   const BwdLds lds{{q_lds0, q_lds1}, {o_lds0, o_lds1}, {st_lds0, st_lds1}};
 
   // tiles [u0, u1) hold only rows that see every key of the workgroup; the
@@ -417,6 +454,7 @@ template <int D, bool BF16, bool BAND> struct DqWave {
   using V8 = typename E::V8;
 
   const BwdArgs& a;
+  const BwdSeq& sq;
   int lane, wave, hh;
   int b, hq, qrow, diag;
   int klo, kspan;            // keys k this lane's row sees: 0 <= k - klo <= kspan (unsigned), k < Nk
@@ -431,19 +469,20 @@ template <int D, bool BF16, bool BAND> struct DqWave {
   f32x16 dqt[C::NCB];        // dQ^T, [d][q]
   BwdDma<D, C::BT> dma;
 
-  __device__ __forceinline__ DqWave(const BwdArgs& args, int b_, int hq_, int q0) : a(args), b(b_), hq(hq_) {
+  __device__ __forceinline__ DqWave(const BwdArgs& args, const BwdSeq& seq, int b_, int hq_, int q0)
+      : a(args), sq(seq), b(b_), hq(hq_) {
     lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     hh = lane >> 5;
     qrow = q0 + wave * C::BT + (lane & 31);
-    diag = a.Nk - a.Nq;
+    diag = sq.nk - sq.nq;
     nsteps = 0;
     j0 = 0;
     const bool has_l = BAND && a.wl >= 0, has_r = BAND && a.wr >= 0;
     klo = has_l ? qrow + diag - a.wl : -(1 << 29);
     kspan = (has_r ? qrow + diag + a.wr : (1 << 29)) - klo;
-    const bool live = qrow < a.Nq;
-    const size_t r = ((static_cast<size_t>(b) * a.Nq + qrow) * a.Hq + hq) * D + 8 * hh;
+    const bool live = qrow < sq.nq;
+    const size_t r = ((sq.q_row0 + qrow) * a.Hq + hq) * D + 8 * hh;
     const T* qp = reinterpret_cast<const T*>(a.q) + r;
     const T* op = reinterpret_cast<const T*>(a.dout) + r;
 #pragma unroll
@@ -457,10 +496,10 @@ template <int D, bool BF16, bool BAND> struct DqWave {
 #pragma unroll
     for (int cb = 0; cb < C::NCB; ++cb) dqt[cb] = f32x16{};
     kpitch = static_cast<uint32_t>(a.Hkv) * D * 2;
-    const size_t head = ((static_cast<size_t>(b) * a.Nk) * a.Hkv + hq / a.group) * D * 2;
+    const size_t head = (sq.k_row0 * a.Hkv + hq / a.group) * D * 2;
     kg = reinterpret_cast<const char*>(a.k) + head;
     vg = reinterpret_cast<const char*>(a.v) + head;
-    valid = static_cast<int64_t>(a.Nk - 1) * kpitch + D * 2;
+    valid = static_cast<int64_t>(sq.nk - 1) * kpitch + D * 2;
     dma.init(kpitch, wave, lane);
   }
 
@@ -507,7 +546,7 @@ template <int D, bool BF16, bool BAND> struct DqWave {
       float pr = exp2_fast(__builtin_fmaf(s[r], a.sl2, -lse2));
       if (MASK) {
         const int kk = j * C::BT + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const bool hide = kk >= a.Nk || (BAND && static_cast<uint32_t>(kk - klo) > static_cast<uint32_t>(kspan));
+        const bool hide = kk >= sq.nk || (BAND && static_cast<uint32_t>(kk - klo) > static_cast<uint32_t>(kspan));
         pr = hide ? 0.f : pr;
       }
       ds[r] = pr * (dp[r] - dsum);
@@ -547,8 +586,8 @@ template <int D, bool BF16, bool BAND> struct DqWave {
   }
 
   __device__ __forceinline__ void finish() const {
-    if (qrow >= a.Nq) return;
-    T* dqp = reinterpret_cast<T*>(a.dq) + ((static_cast<size_t>(b) * a.Nq + qrow) * a.Hq + hq) * D;
+    if (qrow >= sq.nq) return;
+    T* dqp = reinterpret_cast<T*>(a.dq) + ((sq.q_row0 + qrow) * a.Hq + hq) * D;
     typedef T T4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int cb = 0; cb < C::NCB; ++cb)
@@ -586,19 +625,21 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
   const int hq = hb % a.Hq;
   const int b = hb / a.Hq;
   const int q0 = qt * C::WROWS;
-  DqWave<D, BF16, BAND> w(a, b, hq, q0);
+  const BwdSeq sq(a, b);
+  if (q0 >= sq.nq) return;   // a packed sequence shorter than the grid: uniform, before any barrier
+  DqWave<D, BF16, BAND> w(a, sq, b, hq, q0);
   const BwdLds lds{{k_lds0, k_lds1}, {v_lds0, v_lds1}, {nullptr, nullptr}};
 
   // key tiles [j0, nsteps) hold a key some row of the workgroup sees; tiles
   // [u0, u1) hold only keys every row sees (below Nk); the others are masked
-  const int last = min(q0 + C::WROWS, a.Nq) - 1;
+  const int last = min(q0 + C::WROWS, sq.nq) - 1;
   const bool has_l = BAND && a.wl >= 0, has_r = BAND && a.wr >= 0;
   const int ka = has_l ? max(0, q0 + w.diag - a.wl) : 0;
-  const int kb = has_r ? min(a.Nk - 1, last + w.diag + a.wr) : a.Nk - 1;
+  const int kb = has_r ? min(sq.nk - 1, last + w.diag + a.wr) : sq.nk - 1;
   w.j0 = ka / C::BT;
   w.nsteps = kb >= ka ? kb / C::BT + 1 : w.j0;
   const int ua = has_l ? max(0, last + w.diag - a.wl) : 0;
-  const int ub = min(a.Nk - 1, has_r ? q0 + w.diag + a.wr : a.Nk - 1);
+  const int ub = min(sq.nk - 1, has_r ? q0 + w.diag + a.wr : sq.nk - 1);
   const int u0 = min(w.nsteps, max(w.j0, (ua + C::BT - 1) / C::BT));
   const int u1 = max(u0, min(w.nsteps, ub >= 0 ? (ub + 1) / C::BT : 0));
 

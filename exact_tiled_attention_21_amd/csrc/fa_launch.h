@@ -71,6 +71,12 @@ struct BwdArgs {
   // -1 leaves that side open. Causal is wl = -1, wr = 0.
   int wl, wr;
   int hb_kv, hb_q;   // heads per block of the heaviest-first causal orders (dK/dV, dQ)
+  // packed variable-length batch (cu_q non-null): q/o/dout/dq are [total_q][Hq][d],
+  // k/v/dk/dv [total_k][Hkv][d], lse [Hq][total_q]; sequence b owns rows
+  // cu_q[b] .. cu_q[b+1] and cu_k[b] .. cu_k[b+1]; Nq, Nk are the longest counts
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
 };
 
 // Heads per block for blocked_order: as many (batch, head) pairs as keep

@@ -242,6 +242,28 @@ fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void*
                         int Hkv, int d, int window_left, int window_right, int causal, float scale,
                         fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Attention backward pass over a packed batch of variable-length sequences:
+ * the gradients of fa_fwd_varlen's result (same packing, prefix sums and
+ * bottom-right causal mask per sequence).
+ *   q, o, dout, dq : [total_q][Hq][d]; k, v, dk, dv: [total_k][Hkv][d]; `dtype`.
+ *   lse            : float32 [Hq][total_q], as fa_fwd_varlen writes it.
+ *   cu_seqlens_q,
+ *   cu_seqlens_k   : device int32 [B + 1], as for fa_fwd_varlen.
+ *   max_seqlen_q,
+ *   max_seqlen_k   : at least every sequence's query / key count (they size the
+ *                    grid and the workspace; longer sequences are clipped).
+ *   workspace      : fa_bwd_workspace_bytes(B, max_seqlen_q, Hq) bytes.
+ * Rows of dq, dk, dv outside every sequence are not written. Status:
+ * FA_ERR_NULLPTR for a NULL prefix-sum array, FA_ERR_ALIGN for a misaligned one,
+ * FA_ERR_SHAPE for B, max_seqlen_q or max_seqlen_k < 1, otherwise as fa_bwd.
+ */
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, const int* cu_seqlens_q,
+                        const int* cu_seqlens_k, int B, int max_seqlen_q, int max_seqlen_k, int total_q,
+                        int total_k, int Hq, int Hkv, int d, int causal, float scale, fa_dtype dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* fa_status_str(fa_status status);
 

@@ -186,3 +186,20 @@ def test_bwd_window_rejects_invalid_windows(lib, wl, wr, status):
     wsb = lib.fa_bwd_workspace_bytes(1, 8, 2)
     assert lib.fa_bwd_window(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8, 2, 1, 64, wl, wr, 0,
                              0.125, 1, FAKE, wsb, None) == status
+
+
+def bwd_varlen(lib, q=FAKE, cq=FAKE, ck=FAKE, B=2, mq=8, mk=8, tq=16, tk=16, Hq=2, Hkv=1, d=64, ws=FAKE,
+               wsb=None, do=FAKE):
+    if wsb is None:
+        wsb = lib.fa_bwd_workspace_bytes(max(B, 1), max(mq, 1), Hq)
+    return lib.fa_bwd_varlen(q, FAKE, FAKE, FAKE, FAKE, do, FAKE, FAKE, FAKE, cq, ck, B, mq, mk, tq, tk, Hq, Hkv,
+                             d, 0, 0.125, 1, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cq=None), 1), (dict(ck=None), 1), (dict(q=None), 1), (dict(do=None), 1), (dict(ws=None), 1),
+    (dict(B=0), 2), (dict(mq=0), 2), (dict(mk=0), 2), (dict(tq=0), 2), (dict(Hq=3, Hkv=2), 3), (dict(d=40), 4),
+    (dict(cq=FAKE + 2), 9), (dict(ck=FAKE + 1), 9), (dict(wsb=8), 7),
+])
+def test_bwd_varlen_rejects_invalid_arguments(lib, kw, status):
+    assert bwd_varlen(lib, **kw) == status
