@@ -397,7 +397,7 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
 };
 
 template <int D, bool BF16, bool BAND>
-__global__ __launch_bounds__(BwdCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(BwdCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1, D <= 64 ? 2 : 1)))
 void fa_bwd_dkdv_kernel(const BwdArgs a) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) char q_lds0[C::TILEQ];
@@ -602,7 +602,7 @@ template <int D, bool BF16, bool BAND> struct DqWave {
 };
 
 template <int D, bool BF16, bool BAND>
-__global__ __launch_bounds__(BwdCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1, D <= 128 ? 2 : 1)))
+__global__ __launch_bounds__(BwdCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : D <= 128 ? 2 : 1, D <= 64 ? 3 : D <= 128 ? 2 : 1)))
 void fa_bwd_dq_kernel(const BwdArgs a) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) char k_lds0[C::TILE];
