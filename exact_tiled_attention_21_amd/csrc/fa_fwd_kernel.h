@@ -19,9 +19,15 @@
 // j-1; S_j = K_j Q^T on MFMA; softmax; O += V_j P_j on MFMA; barrier. Each
 // tile's loads have a whole step to land. For d <= 128 the kernel fits in 256
 // registers, so two workgroups share a CU and each SIMD can interleave one
-// wave's exponentials with the other wave's matrix products. The running max is only moved when a row's max grows by more than
-// 2^kLazy (in log2 units): P then stays below 2^kLazy and the result is
-// unchanged, since O and the row sum share whichever reference max is used.
+// wave's exponentials with the other wave's matrix products.
+//
+// The reference max m used in P = exp2(s * scale * log2(e) - m) need not be
+// the running max: O and the row sum share it, so the result is the same for
+// any m as long as P stays in range. Masked tiles and the first unmasked tile
+// take the tile's row max and move m when it grows by more than 2^kLazy.
+// Unmasked tiles skip the row max altogether: they form P against the current
+// m and take the (rare) max-and-rebase path only when some lane's sum of the
+// tile's probabilities exceeds kSumCap, which bounds every P of the tile.
 #pragma once
 
 #include "fa_device.h"
@@ -49,7 +55,8 @@ template <int D> struct FwdCfg {
   static_assert(TILE_BYTES % 1024 == 0, "tile must split into whole DMA pieces");
 };
 
-constexpr float kLazy = 8.0f;   // log2 of the largest unnormalised probability kept
+constexpr float kLazy = 8.0f;      // a tile's max moves m when it exceeds m by this (log2 units)
+constexpr float kSumCap = 16384.f;  // larger per-lane tile sums of P redo the tile after a rebase
 
 // The sequence one workgroup works on: its query and key counts, the first
 // rows of its Q/O and K/V in the (padded or packed) tensors, and the index of
@@ -87,15 +94,17 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
   float sl2;
   V8 qf[C::NS];
   f32x16 oacc[C::NCB];
-  float m_run, l_part;
+  // running reference max (log2 units); per-lane partial row sums of the rounded
+  // probabilities (O's normaliser) and, for bf16, of the unrounded ones (the LSE's)
+  float m_run, l_part, l_exact;
   // DMA
   const char* kg;
   const char* vg;
   uint32_t rowbytes;
   int64_t valid;
   uint32_t goff[C::NDMA];
-  // LDS read offsets
-  uint32_t kro, kxo, vb0, vb1, vx0, vx1;
+  // LDS read offsets of this lane's fragments: K slice s, V^T c-block cb (low and high 4 keys)
+  uint32_t kofs[C::NS], vlo[C::NCB], vhi[C::NCB];
 
   // first key row i sees, and one past its last (band and cache bounds)
   __device__ __forceinline__ int lbound(int i) const {
@@ -162,23 +171,32 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
       goff[i] = r * rowbytes + ((pch ^ Swz<D>::f(r)) << 4);
     }
 
-    // LDS read offsets (the swizzle only sees the low 4 row bits)
+    // LDS read offsets (the swizzle only sees the low 4 row bits), computed once:
+    // one register each saves an ALU op per fragment read in the loop
     // K: row 32kb + ln32, chunk (2s | hh) ^ swz(ln32) -> byte (kxo ^ 32s) + row offset
-    kro = ln32 * (D * 2);
-    kxo = (static_cast<uint32_t>(hh) ^ Swz<D>::f(ln32)) << 4;
+    const uint32_t kro = ln32 * (D * 2);
+    const uint32_t kxo = (static_cast<uint32_t>(hh) ^ Swz<D>::f(ln32)) << 4;
     // V: rows 16t + vrow0 (+8), chunk (4cb + vxl) ^ swz(row) -> byte (vx ^ 64cb) + row offset
     const uint32_t vj = lane & 15, vcb = (lane >> 4) & 1;
     const uint32_t vrow0 = 4 * hh + (vj >> 2), vrow1 = vrow0 + 8;
     const uint32_t vxl = 2 * vcb + ((vj & 3) >> 1);
-    vx0 = (vxl ^ Swz<D>::f(vrow0)) << 4;
-    vx1 = (vxl ^ Swz<D>::f(vrow1)) << 4;
-    vb0 = vrow0 * (D * 2) + 8 * (vj & 1);
-    vb1 = vrow1 * (D * 2) + 8 * (vj & 1);
+    const uint32_t vx0 = (vxl ^ Swz<D>::f(vrow0)) << 4;
+    const uint32_t vx1 = (vxl ^ Swz<D>::f(vrow1)) << 4;
+    const uint32_t vb0 = vrow0 * (D * 2) + 8 * (vj & 1);
+    const uint32_t vb1 = vrow1 * (D * 2) + 8 * (vj & 1);
+#pragma unroll
+    for (int i = 0; i < C::NS; ++i) kofs[i] = (kxo ^ (32u * i)) + kro;
+#pragma unroll
+    for (int cb = 0; cb < C::NCB; ++cb) {
+      vlo[cb] = (vx0 ^ (64u * cb)) + vb0;
+      vhi[cb] = (vx1 ^ (64u * cb)) + vb1;
+    }
 
 #pragma unroll
     for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] = f32x16{};
     m_run = kNegInf;
     l_part = 0.f;
+    l_exact = 0.f;
   }
 
   __device__ __forceinline__ void dma(const char* base, int tile, char* lds) const {
@@ -194,15 +212,14 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
             r, (__attribute__((address_space(3))) void*)(lds + (i * C::NW + wave) * 1024), 16, goff[i], 0, 0, 0);
   }
 
-  // LDS fragment addresses: the XOR depends on the lane and the d slice, so
-  // each one costs one ALU op; keeping them all live would cost 16 registers.
+  // LDS fragments: K (A operand of S^T) and V^T (A operand of O^T) at precomputed offsets
   __device__ __forceinline__ V8 kfrag(const char* kt, int kb, int s) const {
-    const uint32_t off = kb * 32 * (D * 2) + ((kxo ^ (32u * s)) + kro);
+    const uint32_t off = kb * 32 * (D * 2) + kofs[s];
     return lds_read_v8<V8>(kt, off);
   }
   __device__ __forceinline__ V8 vfrag(const char* vt, int cb, int t) const {
-    const uint32_t lo = t * 16 * (D * 2) + ((vx0 ^ (64u * cb)) + vb0);
-    const uint32_t hi = t * 16 * (D * 2) + ((vx1 ^ (64u * cb)) + vb1);
+    const uint32_t lo = t * 16 * (D * 2) + vlo[cb];
+    const uint32_t hi = t * 16 * (D * 2) + vhi[cb];
     return __builtin_bit_cast(V8, __builtin_shufflevector(lds_read_tr(vt, lo), lds_read_tr(vt, hi),
                                                           0, 1, 2, 3, 4, 5, 6, 7));
   }
@@ -261,18 +278,25 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
       // 1 when this row keeps its reference (also for a row still at -inf), 0 when it had none
       const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m_run - m_new);
       l_part *= alpha;
+      if (BF16) l_exact *= alpha;
 #pragma unroll
       for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] *= alpha;
       m_run = m_new;
     }
   }
-  // probabilities of a tile (as MFMA B operands, rounded to the element type) and
-  // their row sum, accumulated in fp32 from the unrounded values: summing the
-  // rounded bf16 values would put up to 2^-9 relative error into the LSE
+  // probabilities of a tile against the reference max, as MFMA B operands rounded
+  // to the element type. O is normalised by the sum of the rounded values, so its
+  // weights are the rounded probabilities divided by their own total and a
+  // dominant key carries no rounding error into O. fp16: that sum is formed here
+  // (two values per v_dot2, fp32 accumulate), is within 2^-11 of the unrounded one
+  // and also serves the LSE. bf16: the unrounded fp32 values are summed here for
+  // the LSE (the rounded sum can be 2^-9 off) and the rounded sum is formed by
+  // rounded_sum() once the P V products are issued. Either return value bounds
+  // every probability of the tile.
   template <bool MASK>
-  __device__ __forceinline__ void probs(const SA& sacc, PF& pf) {
+  __device__ __forceinline__ float probs(const SA& sacc, PF& pf) const {
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-    float psum[4] = {0.f, 0.f, 0.f, 0.f};
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
       f32x16 tmp;
@@ -281,12 +305,30 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
         const float sv = sacc[t >> 1][8 * (t & 1) + i];
         float p = exp2_fast(__builtin_fmaf(sv, sl2, -m_use));
         if (MASK) p = (sv == kNegInf) ? 0.f : p;
-        psum[i & 3] += p;
+        if (BF16) ps[i & 3] += p;
         tmp[i] = p;
       }
       pf[t] = to_v8<BF16>(tmp, 0);
+      if (!BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ps[i & 1] = dot2_ones<BF16>(pf[t], i, ps[i & 1]);
+      }
     }
-    l_part += (psum[0] + psum[1]) + (psum[2] + psum[3]);
+    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  }
+  // this lane's sum of the rounded probabilities of a tile (bf16)
+  __device__ __forceinline__ float rounded_sum(const PF& pf) const {
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rs[i] = dot2_ones<BF16>(pf[t], i, rs[i]);
+    return (rs[0] + rs[1]) + (rs[2] + rs[3]);
+  }
+  // adds a tile's sums: `ps` from probs(), the rounded sum (bf16) after the P V products
+  __device__ __forceinline__ void add_sum(float ps) {
+    if (BF16) l_exact += ps;
+    else l_part += ps;
   }
 
   // O += V_j P_j, with the transposing reads of V kVPre MFMAs ahead through a
@@ -318,7 +360,6 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
   // the O accumulators keep their registers across the loop.
   template <int ST, bool TAIL>
   __device__ __forceinline__ void step(int j, const FwdLds<D>& lds) {
-    asm volatile("" : "+v"(kxo), "+v"(vx0), "+v"(vx1));
     if (j + 1 < jhi) {
       dma(kg, j + 1, lds.k[ST ^ 1]);
       dma(vg, j + 1, lds.v[ST ^ 1]);
@@ -327,9 +368,17 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
       SA sacc;
       PF pf;
       qk(lds.k[ST], sacc);
-      rebase(rowmax<false>(sacc, j));
-      probs<false>(sacc, pf);
+      // no row max: redo the tile after a rebase only if a probability may be
+      // out of range (or m is not set yet); a NaN sum also takes that path
+      float ps = probs<false>(sacc, pf);
+      const bool need = !(ps <= kSumCap) || m_run == kNegInf;
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+        rebase(rowmax<false>(sacc, j));
+        ps = probs<false>(sacc, pf);
+      }
+      add_sum(ps);
       pv(lds.v[ST], pf);
+      if (BF16) l_part += rounded_sum(pf);
     } else {
       // masked tiles: every wave computes them with the element mask, so the
       // step stays straight-line code (a wave that sees none of the tile gets
@@ -338,8 +387,9 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
       PF pf;
       qk(lds.k[ST], sacc);
       rebase(rowmax<true>(sacc, j));
-      probs<true>(sacc, pf);
+      add_sum(probs<true>(sacc, pf));
       pv(lds.v[ST], pf);
+      if (BF16) l_part += rounded_sum(pf);
     }
     __syncthreads();
   }
@@ -347,6 +397,7 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
   // O = O / l, LSE = m + log(l); rows with no visible key give 0 and -inf
   __device__ __forceinline__ void finish(int hq) {
     const float l = halves_sum(l_part);
+    const float l_lse = BF16 ? halves_sum(l_exact) : l;
     if (qrow >= sq.nq) return;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     T* op = reinterpret_cast<T*>(a.o) + ((sq.q_row0 + qrow) * a.Hq + hq) * D;
@@ -363,7 +414,7 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
     }
     if (a.lse != nullptr && hh == 0)
       a.lse[sq.lse0 + qrow] =
-          l > 0.f ? (m_run + __log2f(l)) * kLn2 : kNegInf;
+          l_lse > 0.f ? (m_run + __log2f(l_lse)) * kLn2 : kNegInf;
   }
 };
 
