@@ -90,7 +90,7 @@ fa_status check_common(const void* q, const void* k, const void* v, void* o, con
 
 size_t pad256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// each requested chunk is processed as up to this many sub-chunks, each with its
+// each requested split is processed as up to this many parts, each with its
 // own partial (the workspace is sized for the maximum)
 constexpr int kSubPerChunk = 4;
 // single-wave workgroups that give the chip about one round (256 CUs x 4 SIMDs)

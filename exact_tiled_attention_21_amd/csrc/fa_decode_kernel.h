@@ -7,17 +7,23 @@
 // every chunk in parallel while writing one extra scalar per row and chunk
 // (the log-sum-exp), then combine.
 //
-// Split kernel: each chunk is processed as 1, 2 or 4 sub-chunks (enough to give
-// the chip about one round of waves), one single-wave workgroup per (sub-chunk,
-// KV head, batch[, row block]). The query rows of the
-// whole GQA group (Hq/Hkv heads x Nq positions, at most 32 per row block) share
-// the sub-chunk's K/V, which is therefore read from HBM once. The wave streams
-// its 32-key tiles with fully coalesced 16-byte loads into a ring of two tiles
-// in registers, stages each tile through its own swizzled LDS tiles (K for the
-// A operand, V for the transposing read), and writes one normalised fp32
-// partial and its log-sum-exp per row; the combine kernel merges the
-// sub-chunk partials of every chunk with the other chunks'. No barriers: up to
-// four such waves share a CU, one per SIMD.
+// Split kernel: the keys are cut into 32-key tiles and dealt out to the parts
+// round-robin: part p of P*S parts takes tiles p, p + P*S, ... (S requested
+// splits, each dealt out as P = 1, 2 or 4 parts so that the chip gets about one
+// round of waves). Any partition of the keys merges exactly, and this one makes
+// the parts of a sequence read one dense window of the cache at a time (all
+// parts step through neighbouring tiles together), which keeps the DRAM pages
+// open: with contiguous chunks every part streams its own region. One
+// single-wave workgroup per (part, KV head, batch[, row block]); the query rows
+// of the whole GQA group (Hq/Hkv heads x Nq positions, at most 32 per row block)
+// share the part's K/V, which is therefore read from HBM once. The wave loads
+// each tile with fully coalesced, non-temporal 16-byte loads into registers
+// (one tile ahead: about 16 MiB in flight chip-wide is enough for the HBM rate,
+// more only thins out the DRAM locality), stages it through its own swizzled
+// LDS tiles (K for the A operand, V for the transposing read), and writes one
+// normalised fp32 partial and its log-sum-exp per row; the combine kernel
+// merges the partials. No barriers: up to four such waves share a CU, one per
+// SIMD.
 //
 // Paged cache ("flash-attention-v100" README, flash_attn_with_kvcache: a block
 // table maps each sequence's logical key blocks to pages of a shared pool, and
@@ -42,10 +48,13 @@ template <int D> struct DecCfg {
   static constexpr int CPR = D / 8;               // 16-byte chunks per row
   static constexpr int NCH = BC * CPR / 64;       // 16-byte chunks per lane per tensor per tile
   static constexpr int TILE = BC * D * 2;         // bytes of one K or V tile
-  static constexpr int NSLOT = (D <= 128) ? 2 : 1;  // tiles in flight in registers
 };
 
-// One wave per workgroup: it streams the keys of one sub-chunk.
+// Cache policy of the K/V loads: non-temporal (every cache byte is read exactly
+// once per step, so it should not displace anything).
+constexpr int kNonTemporal = 2;
+
+// One wave per workgroup: it streams the tiles of one part.
 template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
   using C = DecCfg<D>;
   using E = Elem<BF16>;
@@ -57,7 +66,8 @@ template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
   int lane, hh;
   bool rvalid;
   int b, g, L;                  // batch, KV head, keys of this sequence
-  int ri, rhq, diag, i_first, k_lo, k_hi, ntile;
+  int ri, rhq, diag, i_first, k_hi, ntile;
+  int part, nparts;             // this part's index and the number of parts (tile stride)
   float sl2;
   V8 qf[C::NS];
   f32x16 oacc[C::NCB];
@@ -69,7 +79,7 @@ template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
   uint32_t goff;                // this lane's first 16-byte piece of a tile (coalesced rows)
   uint32_t kro, kxo, vb0, vb1, vx0, vx1;   // LDS fragment read offsets
 
-  __device__ __forceinline__ DecWave(const DecodeArgs& args, int part, int g_, int rb, int b_)
+  __device__ __forceinline__ DecWave(const DecodeArgs& args, int part_, int g_, int rb, int b_)
       : a(args), b(b_), g(g_) {
     lane = threadIdx.x & 63;
     hh = lane >> 5;
@@ -88,23 +98,19 @@ template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) qf[s] = rvalid ? *reinterpret_cast<const V8*>(qp + 16 * s) : V8{};
 
-    // keys of this sub-chunk: chunk part / sub_per, piece part % sub_per; chunks
-    // of ceil(L / S) keys and sub-chunks of ceil(chunk / sub_per) keys, both
-    // rounded up to 32; clipped by the chunk, the sequence length and (causal)
-    // the last row
-    const int S = a.splits / a.sub_per;
-    const int chunk = ((L + S - 1) / S + 31) / 32 * 32;
-    const int sub = ((chunk + a.sub_per - 1) / a.sub_per + 31) / 32 * 32;
-    const int c_lo = (part / a.sub_per) * chunk;
-    const int c_hi = min(L, c_lo + chunk);
-    k_lo = c_lo + (part % a.sub_per) * sub;
-    k_hi = min(c_hi, k_lo + sub);
+    // tiles of this part: the keys are cut into 32-key tiles and part p of the
+    // nparts parts takes tiles p, p + nparts, p + 2 nparts, ... below k_hi (the
+    // sequence length, or for causal one past the last row's last key)
+    part = part_;
+    nparts = a.splits;
     i_first = (rb * 32) / a.group;
+    k_hi = L;
     if (CAUSAL) {
       const int i_last = (min(R, rb * 32 + 32) - 1) / a.group;
-      k_hi = min(k_hi, i_last + diag + 1);
+      k_hi = max(0, min(k_hi, i_last + diag + 1));
     }
-    ntile = k_hi > k_lo ? (k_hi - k_lo + C::BC - 1) / C::BC : 0;
+    const int tiles = (k_hi + C::BC - 1) / C::BC;
+    ntile = part < tiles ? (tiles - part + nparts - 1) / nparts : 0;
 
     rowbytes = static_cast<uint32_t>(a.Hkv) * D * 2;
     const size_t head_off = ((PAGED ? 0 : static_cast<size_t>(b) * a.Nk * a.Hkv) + g) * D * 2;
@@ -129,12 +135,15 @@ template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
     l_part = 0.f;
   }
 
+  // first key of this part's tile t
+  __device__ __forceinline__ int key0_of(int t) const { return (part + t * nparts) * C::BC; }
+
   // K and V rows of tile t into registers, 16 lanes per 256-byte row (coalesced);
   // rows past the sequence read as zero through the buffer bounds check. A
   // paged tile lies in one page; a page index outside the pool reads as zeros
   // rather than leaving the pool.
   __device__ __forceinline__ void load(int t, Stage& ks, Stage& vs) const {
-    const int key0 = k_lo + t * C::BC;
+    const int key0 = key0_of(t);
     int64_t off, rem;
     if (PAGED) {
       const int rows = min(C::BC, L - key0);
@@ -156,8 +165,8 @@ template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
 #pragma unroll
     for (int i = 0; i < C::NCH; ++i) {
       const uint32_t o = goff_of(i);
-      ks[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
-      vs[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+      ks[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kNonTemporal));
+      vs[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, kNonTemporal));
     }
   }
   // piece i of a tile is 16-byte chunk c = lane + 64 i of the tile: row c / CPR, chunk c % CPR
@@ -190,7 +199,7 @@ template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
   // one 32-key tile from the LDS tiles: scores, online softmax, O += V P
   template <bool MASK>
   __device__ __forceinline__ void tile(int t, const char* kt, const char* vt) {
-    const int k0 = k_lo + t * C::BC;
+    const int k0 = key0_of(t);
     f32x16 sacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) sacc = E::mfma(kfrag(kt, s), qf[s], sacc);
@@ -234,7 +243,7 @@ template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
     }
   }
   __device__ __forceinline__ void tile_any(int t, const char* kt, const char* vt) {
-    const int k0 = k_lo + t * C::BC;
+    const int k0 = key0_of(t);
     if ((k0 + C::BC > k_hi) || (CAUSAL && k0 + C::BC - 1 > i_first + diag)) tile<true>(t, kt, vt);
     else tile<false>(t, kt, vt);
   }
@@ -258,35 +267,26 @@ __global__ __launch_bounds__(64) void fa_decode_split_kernel(const DecodeArgs a)
 
   // the KV heads of one key range are consecutive in dispatch order: their rows
   // interleave in memory, so reading them together keeps DRAM pages open
-  const int part = blockIdx.y;            // chunk * sub_per + piece
+  const int part = blockIdx.y;            // one of the a.splits parts
   const int g = blockIdx.x % a.Hkv;
   const int rb = blockIdx.x / a.Hkv;
   const int b = blockIdx.z;
   W w(a, part, g, rb, b);
 
-  // tiles t of the sub-chunk; the loads run NSLOT tiles ahead in registers and
-  // are issued for every tile slot (past the end they read zeros), so each
-  // tile's wait covers exactly its own loads
-  typename W::Stage ks0, vs0, ks1, vs1;
-  w.load(0, ks0, vs0);
-  if (C::NSLOT == 2) w.load(1, ks1, vs1);
-  for (int t = 0; t < w.ntile; t += C::NSLOT) {
-    w.stage(ks0, vs0, kt, vt);
+  // tiles t of this part: the loads of tile t + 1 are issued once tile t sits in
+  // LDS, so they overlap tile t's products; loads past the end read zeros, so
+  // each tile's wait covers exactly its own loads
+  typename W::Stage ks, vs;
+  w.load(0, ks, vs);
+  for (int t = 0; t < w.ntile; ++t) {
+    w.stage(ks, vs, kt, vt);
     wave_lds_sync();
-    w.load(t + C::NSLOT, ks0, vs0);
+    w.load(t + 1, ks, vs);
     w.tile_any(t, kt, vt);
     wave_lds_sync();
-    if (C::NSLOT == 2) {
-      if (t + 1 >= w.ntile) break;
-      w.stage(ks1, vs1, kt, vt);
-      wave_lds_sync();
-      w.load(t + 3, ks1, vs1);
-      w.tile_any(t + 1, kt, vt);
-      wave_lds_sync();
-    }
   }
 
-  // normalised partial and its log2-sum-exp; a sub-chunk with no visible key
+  // normalised partial and its log2-sum-exp; a part with no visible key
   // writes O = 0, LSE = -inf
   const float l = halves_sum(w.l_part);
   if (!w.rvalid) return;
@@ -307,7 +307,9 @@ __global__ __launch_bounds__(64) void fa_decode_split_kernel(const DecodeArgs a)
 
 // One row of the output per D/4 threads: O = sum_s w_s O_s with
 // w_s = exp(LSE_s - LSE), LSE = log sum_s exp(LSE_s) (log2 domain inside).
-// Splits are taken 16 at a time with every load of a batch issued at once.
+// One pass: the LSEs and partial outputs of 16 parts are loaded together and
+// merged against a running max, so a step with at most 16 parts waits on memory
+// once.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void fa_decode_combine_kernel(const DecodeArgs a) {
   using T = typename Elem<BF16>::T;
@@ -318,36 +320,38 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(const DecodeArgs
   const int row = blockIdx.x * RPB + threadIdx.x / TPR;
   if (row >= rows) return;
   const int c4 = (threadIdx.x % TPR) * 4;
-  const size_t stride = static_cast<size_t>(rows);   // elements between splits
+  const size_t stride = static_cast<size_t>(rows);   // elements between parts
   float mx = kNegInf;
-  for (int s0 = 0; s0 < a.splits; s0 += SB) {
-    float l[SB];
-#pragma unroll
-    for (int i = 0; i < SB; ++i) l[i] = (s0 + i < a.splits) ? a.part_lse[(s0 + i) * stride + row] : kNegInf;
-#pragma unroll
-    for (int i = 0; i < SB; ++i) mx = fmaxf(mx, l[i]);
-  }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float tot = 0.f;
-  if (mx != kNegInf) {
-    for (int s0 = 0; s0 < a.splits; s0 += SB) {
-      float l[SB];
-      f32x4 o[SB];
+  for (int s0 = 0; s0 < a.splits; s0 += SB) {
+    float l[SB];
+    f32x4 o[SB];
 #pragma unroll
-      for (int i = 0; i < SB; ++i) {
-        const bool ok = s0 + i < a.splits;
-        l[i] = ok ? a.part_lse[(s0 + i) * stride + row] : kNegInf;
-        o[i] = ok ? *reinterpret_cast<const f32x4*>(a.part_o + ((s0 + i) * stride + row) * D + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int i = 0; i < SB; ++i) {
-        const float wgt = exp2_fast(l[i] - mx);   // 0 for an empty chunk (-inf)
-        tot += wgt;
-        acc += wgt * o[i];
-      }
+    for (int i = 0; i < SB; ++i) {
+      const bool ok = s0 + i < a.splits;
+      l[i] = ok ? a.part_lse[(s0 + i) * stride + row] : kNegInf;
+      o[i] = ok ? *reinterpret_cast<const f32x4*>(a.part_o + ((s0 + i) * stride + row) * D + c4)
+                : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    acc *= 1.f / tot;
+    float mb = kNegInf;
+#pragma unroll
+    for (int i = 0; i < SB; ++i) mb = fmaxf(mb, l[i]);
+    if (mb == kNegInf) continue;   // no part of this batch saw a key
+    if (mb > mx) {                 // move the reference: earlier weights shrink (to 0 from -inf)
+      const float r = exp2_fast(mx - mb);
+      acc *= r;
+      tot *= r;
+      mx = mb;
+    }
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      const float wgt = exp2_fast(l[i] - mx);   // 0 for a part with no key (-inf)
+      tot += wgt;
+      acc += wgt * o[i];
+    }
   }
+  if (mx != kNegInf) acc *= 1.f / tot;
   // row = (b * Hq + hq) * Nq + i  ->  o[b][i][hq][:]
   const int i = row % a.Nq;
   const int bh = row / a.Nq;

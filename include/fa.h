@@ -7,8 +7,8 @@
  *                      reaches device memory (variants: fa_fwd_window,
  *                      fa_fwd_varlen);
  *   fa_decode_splitkv  the same result for short query blocks, with the keys
- *                      split into chunks that are processed in parallel and a
- *                      second kernel that merges the per-chunk results
+ *                      split into parts that are processed in parallel and a
+ *                      second kernel that merges the per-part results
  *                      (variant: fa_decode_splitkv_paged);
  *   fa_bwd             the gradients dQ, dK, dV of the forward pass, again
  *                      without storing the score matrix.
@@ -21,8 +21,8 @@
  *     the bottom-right corner (Changelog 2.1; flash_attn_with_kvcache
  *     docstring); a row that sees no key gets O = 0.
  * Flash-Decoding ("flash attention-2 github" search page; "flash-attention-v100"
- * README, Changelog 2.2): split the keys into chunks, attend to each chunk in
- * parallel while writing one log-sum-exp per row and chunk, then combine.
+ * README, Changelog 2.2): split the keys into parts, attend to each part in
+ * parallel while writing one log-sum-exp per row and part, then combine.
  *
  * Layouts (row-major, head_dim fastest; "ampere_flash_attention_from_scratch"
  * README, Performance Test header [batch_size, seq_len, num_heads, head_dim]):
@@ -129,7 +129,7 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
 
 /*
  * Bytes of device workspace fa_decode_splitkv needs. Each of the num_splits
- * chunks is processed as up to 4 sub-chunks with a partial result each; the
+ * splits is processed as up to 4 parts with a partial result each; the
  * workspace holds float32 partial outputs [4*num_splits][B][Hq][Nq][d]
  * followed by float32 partial LSEs [4*num_splits][B][Hq][Nq], each part
  * padded to 256 bytes. Returns 0 for invalid sizes.
@@ -140,18 +140,20 @@ size_t fa_decode_workspace_bytes(int B, int Nq, int Hq, int d, int num_splits);
  * Split-KV attention (Flash-Decoding) over a contiguous KV cache.
  *   q, o       : [B][Nq][Hq][d]; k_cache, v_cache: [B][Nk][Hkv][d]; all `dtype`.
  *   lse        : float32 [B][Hq][Nq] or NULL.
- *   num_splits : number of key chunks S, 1..FA_MAX_SPLITS. Chunk s covers keys
- *                [s*C, min(Nk, (s+1)*C)) with C = ceil(Nk/S) rounded up to a
- *                multiple of 32; chunks past Nk are empty and weigh nothing.
- *                Each chunk is processed as P = 1, 2 or 4 sub-chunks of
- *                ceil(C/P) keys (rounded up to 32), each by its own
- *                workgroup; P grows when there are few chunks x heads x batch.
+ *   num_splits : number of key splits S, 1..FA_MAX_SPLITS. The keys are cut
+ *                into 32-key tiles; each split is processed as P = 1, 2 or 4
+ *                parts (P grows when there are few splits x heads x batch),
+ *                and part p of the P*S parts takes tiles p, p + P*S,
+ *                p + 2*P*S, ... (tile-interleaved, so the parts read
+ *                neighbouring tiles at the same time). Parts with no tile are
+ *                empty and weigh nothing. The merged result does not depend on
+ *                the partition beyond float32 rounding.
  *                Nk * Hkv * d * 2 must stay below 2^31 (FA_ERR_SHAPE).
  *   causal     : as in fa_fwd (bottom-right aligned against Nk).
  *   workspace  : caller-owned device buffer of at least
  *                fa_decode_workspace_bytes(B, Nq, Hq, d, num_splits) bytes,
  *                16-byte aligned; its contents on entry do not matter.
- * Two kernels are enqueued on `stream`: the per-chunk pass, then the merge.
+ * Two kernels are enqueued on `stream`: the per-part pass, then the merge.
  * The result equals fa_fwd's on the same inputs up to float32 rounding.
  */
 fa_status fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache, void* o,
@@ -176,8 +178,8 @@ fa_status fa_decode_splitkv(const void* q, const void* k_cache, const void* v_ca
  *                   clamped to [0, max_pages_per_seq * page_size]. A sequence
  *                   with no key gets O = 0 and LSE = -inf.
  *   page_size     : a multiple of 32 (>= 32).
- *   num_splits    : as in fa_decode_splitkv, with C = ceil(len_b / S) rounded
- *                   up to 32 computed per sequence from its own length.
+ *   num_splits    : as in fa_decode_splitkv; the tiles of sequence b are those
+ *                   below its own length.
  *   causal        : bottom-right aligned against each sequence's length.
  *   workspace     : fa_decode_workspace_bytes(B, Nq, Hq, d, num_splits) bytes.
  * A contiguous cache [B][Nk][Hkv][d] with per-sequence lengths is the special
