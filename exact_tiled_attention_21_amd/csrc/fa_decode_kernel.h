@@ -249,15 +249,6 @@ template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
   }
 };
 
-// LDS writes of this wave must land before its reads, and its reads before the
-// next writes: LDS executes one wave's operations in order, so only the
-// compiler must be kept from moving them across this point.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 template <int D, bool BF16, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(64) void fa_decode_split_kernel(const DecodeArgs a) {
   using C = DecCfg<D>;

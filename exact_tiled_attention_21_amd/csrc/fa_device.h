@@ -144,6 +144,15 @@ __device__ __forceinline__ float dot2_ones<true>(bf16x8 x, int i, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(v, one, acc, false);
 }
 
+// LDS writes of a wave must land before its reads of them, and its reads before
+// its next writes: LDS executes one wave's operations in order, so only the
+// compiler must be kept from moving them across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Compile-time LDS stage index passed to generic lambdas.
 template <int N> struct Stage { static constexpr int value = N; };
 

@@ -394,25 +394,45 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
     __syncthreads();
   }
 
-  // O = O / l, LSE = m + log(l); rows with no visible key give 0 and -inf
-  __device__ __forceinline__ void finish(int hq) {
+  // O = O / l, LSE = m + log(l); rows with no visible key give 0 and -inf.
+  // The accumulator gives each lane 4-element pieces of its row, so storing it
+  // directly writes 16 scattered bytes per row and instruction; instead the
+  // wave's 32 x D tile of O goes through its own slice of the (now idle) K/V
+  // LDS stages, and each 16-byte store instruction then writes whole rows.
+  __device__ __forceinline__ void finish(int hq, const FwdLds<D>& lds) {
     const float l = halves_sum(l_part);
     const float l_lse = BF16 ? halves_sum(l_exact) : l;
-    if (qrow >= sq.nq) return;
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    T* op = reinterpret_cast<T*>(a.o) + ((sq.q_row0 + qrow) * a.Hq + hq) * D;
+    // this wave's tile: [32][D] of the element type, 16-byte chunks swizzled by row
+    constexpr int WPS = C::BC / 32;                // waves per LDS stage
+    constexpr uint32_t kRowB = D * 2;
+    const int st = wave / WPS;
+    char* const ot = (st == 0 ? lds.k[0] : st == 1 ? lds.k[1] : st == 2 ? lds.v[0] : lds.v[1]) +
+                     (wave % WPS) * (32 * kRowB);
+    typedef T T4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int cb = 0; cb < C::NCB; ++cb) {
+    for (int cb = 0; cb < C::NCB; ++cb)
 #pragma unroll
       for (int gr = 0; gr < 4; ++gr) {
-        typedef T T4 __attribute__((ext_vector_type(4)));
+        // columns 32cb + 8gr + 4hh .. +3 of row ln32: half hh of chunk 4cb + gr
         T4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = (T)(oacc[cb][4 * gr + e] * inv);
-        *reinterpret_cast<T4*>(op + 32 * cb + 8 * gr + 4 * hh) = w;
+        *reinterpret_cast<T4*>(ot + Swz<D>::off(ln32, 4 * cb + gr) + 8 * hh) = w;
       }
+    wave_lds_sync();
+    // chunk c = 64 i + lane of the tile: row c / (D / 8), 16-byte chunk c % (D / 8)
+    constexpr int CPR = D / 8;
+    T* const obase = reinterpret_cast<T*>(a.o) + (sq.q_row0 * a.Hq + hq) * D;
+#pragma unroll
+    for (int i = 0; i < CPR / 2; ++i) {
+      const uint32_t c = 64 * i + lane;
+      const uint32_t row = c / CPR, x = c % CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ot + Swz<D>::off(row, x));
+      const int r = q0w + static_cast<int>(row);
+      if (r < sq.nq) *reinterpret_cast<u32x4*>(obase + static_cast<size_t>(r) * a.Hq * D + 8 * x) = v;
     }
-    if (a.lse != nullptr && hh == 0)
+    if (a.lse != nullptr && hh == 0 && qrow < sq.nq)
       a.lse[sq.lse0 + qrow] =
           l_lse > 0.f ? (m_run + __log2f(l_lse)) * kLn2 : kNegInf;
   }
@@ -499,7 +519,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fa_fwd
     w.template step<1, true>(j + 1, lds);
   }
   if (j < w.jhi) w.template step<0, true>(j, lds);
-  w.finish(hq);
+  w.finish(hq, lds);
 }
 
 template <int D>
