@@ -126,16 +126,6 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
     diag = sq.nk - sq.nq;
     sl2 = a.sl2;
 
-    // Q fragment (B operand): Q[qrow][16s + 8hh .. +7]; sign-flipped for a negative scale
-    const T* qp = reinterpret_cast<const T*>(a.q) +
-                  ((sq.q_row0 + qrow) * a.Hq + hq) * D + 8 * hh;
-#pragma unroll
-    for (int s = 0; s < C::NS; ++s) {
-      if (qrow < sq.nq) qf[s] = *reinterpret_cast<const V8*>(qp + 16 * s);
-      else qf[s] = V8{};
-      if (a.negate_q) qf[s] = -qf[s];
-    }
-
     // Key extents. Row i sees keys j with i + diag - wl <= j <= i + diag + wr
     // (the band of a sliding window; causal is wl = none, wr = 0), clipped to
     // [0, nk). The first row has the smallest bounds, the last the largest.
@@ -197,6 +187,19 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
     m_run = kNegInf;
     l_part = 0.f;
     l_exact = 0.f;
+  }
+
+  // Q fragment (B operand): Q[qrow][16s + 8hh .. +7], sign-flipped for a negative
+  // scale. All loads are issued before the flip, which waits for them once.
+  __device__ __forceinline__ void load_q(int hq) {
+    const T* qp = reinterpret_cast<const T*>(a.q) +
+                  ((sq.q_row0 + qrow) * a.Hq + hq) * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) qf[s] = qrow < sq.nq ? *reinterpret_cast<const V8*>(qp + 16 * s) : V8{};
+    if (a.negate_q) {
+#pragma unroll
+      for (int s = 0; s < C::NS; ++s) qf[s] = -qf[s];
+    }
   }
 
   __device__ __forceinline__ void dma(const char* base, int tile, char* lds) const {
@@ -482,11 +485,13 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fa_fwd
 
   FwdWave<D, BF16, BAND> w(a, sq, hq, g, qt);
   const FwdLds<D> lds{{k_lds0, k_lds1}, {v_lds0, v_lds1}};
-  // tile j lives in stage (j - jlo) & 1
+  // tile j lives in stage (j - jlo) & 1; the first tile's DMA goes out before
+  // the Q loads, so the prologue waits for one memory latency, not two
   if (w.jhi > w.jlo) {
     w.dma(w.kg, w.jlo, lds.k[0]);
     w.dma(w.vg, w.jlo, lds.v[0]);
   }
+  w.load_q(hq);
   __syncthreads();
   int j = w.jlo;
   // masked tiles before the unmasked run (the left edge of a band); all of
