@@ -70,6 +70,36 @@ def test_head_dims(d, dtype, causal):
     run_full(wid, 2, 200, 333, 6, 2, d, dtype, causal)
 
 
+def ramp_bits(wid, tensor_id, shape, dtype, lo, hi):
+    """N(0,1) samples whose rows along the sequence axis are scaled from lo up to hi,
+    rounded to dtype: scores then grow along the keys, so the running max of every
+    row keeps rising tile after tile."""
+    rng = np.random.default_rng([wid, tensor_id])
+    x = rng.standard_normal(shape, dtype=np.float32)
+    ramp = np.linspace(lo, hi, shape[1], dtype=np.float32)[None, :, None, None]
+    return synthetic.to_bits(x * ramp, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_reference_moves_in_unmasked_tiles(dtype, causal):
+    """Keys scaled up along the sequence (x0.2 to x4, scale 0.5): a row's scores rise
+    by far more than 2^14 in log2 units across the unmasked tiles, so the reference
+    max is moved in the middle of the key loop (a lane's sum of probabilities
+    exceeds the cap and the tile is redone against its own max), not only on the
+    first tile."""
+    B, N, H, d = 1, 1024, 4, 128
+    qb = synthetic.normal_bits(91, 0, (B, N, H, d), dtype)
+    kb = ramp_bits(91, 1, (B, N, H, d), dtype, 0.2, 4.0)
+    vb = synthetic.normal_bits(91, 2, (B, N, H, d), dtype)
+    print(f"[fwd rebase] {dtype} causal={causal}", flush=True)
+    o, lse = attention(to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype), causal=causal, scale=0.5)
+    o_ref, lse_ref = oracle.attention_bits(qb, kb, vb, dtype, causal=causal, scale=0.5)
+    what = f"rising scores {dtype} causal={causal}"
+    cmp.check_o(to_np(o), o_ref, dtype, what)
+    cmp.check_lse(to_np(lse), lse_ref, what)
+
+
 def test_scale_is_used_as_passed():
     run_full(300, 1, 130, 130, 2, 2, 64, "f16", False, scale=0.37)
     run_full(301, 1, 130, 130, 2, 2, 64, "bf16", True, scale=0.0)
