@@ -4,8 +4,11 @@
 One step = one forward pass over the pages' headline workload
 [B=16, N=1024, H=32, d=128] fp16, non-causal (inputs resident in HBM). The line
 also carries the split-KV decode step (split + combine kernels) at
-B=8, Nq=1, Nk=8192, Hq=32, Hkv=8, d=128 bf16 with 16 chunks, and the forward at
-N=4096, each timed the same way. Prints one JSON line.
+B=8, Nq=1, Nk=8192, Hq=32, Hkv=8, d=128 bf16 with 16 splits, the forward at
+N=4096, a packed variable-length batch, the backward pass, and a sweep over the
+pages' other workloads (long sequences causal and not, the sharpened bf16 repeat,
+the GQA head-dim sweep, decode with Nq=8; inputs drawn on the device), each timed
+the same way. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -140,6 +143,63 @@ def cpu_baseline_decode(w, reps_budget_s=3.0):
             "kind": "oracle", "sample": f"{w.name}: the whole step x{reps}, fp64 ({took:.1f} s)"}
 
 
+def device_inputs(w, torch, dev):
+    """Seeded N(0,1) inputs of workload w generated on the device (Q and K times the
+    workload's multiplier), for throughput runs too large to draw on the host."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.wid)
+    dt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+    out = []
+    for shape, mult in zip(w.shapes(), (w.qk_mult, w.qk_mult, 1.0)):
+        x = torch.randn(shape, device=dev, generator=g, dtype=torch.float32)
+        out.append((x * mult).to(dt))
+        del x
+    return out
+
+
+def sweep(args, torch, dev):
+    """Forward throughput over the pages' other workloads (long sequences, causal and
+    not, the sharpened bf16 repeat, the GQA head-dim sweep) and decode with Nq = 8."""
+    import synthetic
+    from exact_tiled_attention_21_amd import attention, decode, decode_workspace_bytes
+    rows = []
+    names = [n for n, w in synthetic.WORKLOADS.items()
+             if not w.decode and (n.startswith("long_") or n.startswith("gqa_"))]
+    for name in names:
+        w = synthetic.WORKLOADS[name]
+        q, k, v = device_inputs(w, torch, dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+        ms = time_steps(lambda i=0: attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse),
+                        max(3, args.steps // 10), 2, torch, min(args.prewarm_s, 0.3))
+        t = w.flops() / (ms * 1e-3) / 1e12
+        row = {"workload": name, "ms": round(ms, 4), "tflops": round(t, 2),
+               "tflops_pages_convention": round(t / 2, 2), "mfma_peak_frac": round(t / PEAK_MFMA_F16, 4)}
+        if w.causal:   # the same time against the un-halved 4 B H N^2 d count
+            row["tflops_unhalved_count"] = round(4.0 * w.B * w.Hq * w.Nq * w.Nk * w.d / (ms * 1e-3) / 1e12, 2)
+        rows.append(row)
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    wd = synthetic.WORKLOADS["decode_bf16_nq8"]
+    sets = []
+    for r in range(4):
+        sets.append(device_inputs(dataclasses.replace(wd, wid=wd.wid + 1000 * r), torch, dev))
+    ws = torch.empty(decode_workspace_bytes(wd.B, wd.Nq, wd.Hq, wd.d, wd.num_splits), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(sets[0][0])
+
+    def dstep(i=0):
+        qq, kk, vv = sets[i % len(sets)]
+        decode(qq, kk, vv, num_splits=wd.num_splits, scale=wd.scale, workspace=ws, out=o)
+
+    msd = time_steps(dstep, max(args.steps, 100), args.warmup, torch, min(args.prewarm_s, 0.3))
+    kv_bytes = 2 * wd.B * wd.Nk * wd.Hkv * wd.d * 2
+    rows.append({"workload": wd.name, "us_per_step": round(msd * 1e3, 2),
+                 "kv_GBps": round(kv_bytes / (msd * 1e-3) / 1e9, 1), "kv_sets_rotated": len(sets)})
+    del sets, ws, o
+    torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +209,7 @@ def main():
     ap.add_argument("--only", choices=["fwd", "headline", "decode", "bwd", "all"], default="all")
     ap.add_argument("--prewarm-s", type=float, default=1.0,
                     help="seconds of untimed launches per workload before its warmup steps")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the sweep over the other workloads")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -232,6 +293,9 @@ def main():
                                 "tokens": tot, "ms": round(msv, 4), "tflops": round(fl / (msv * 1e-3) / 1e12, 2)}
         del qv, kv_, vv_, ov
         torch.cuda.empty_cache()
+
+    if args.only in ("fwd", "all") and not args.no_sweep:
+        result["sweep"] = sweep(args, torch, dev)
 
     # ---- split-KV decode, rotating over KV sets larger than the 256 MB infinity cache
     if args.only in ("decode", "all"):
