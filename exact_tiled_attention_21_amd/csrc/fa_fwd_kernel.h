@@ -95,6 +95,7 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
   // [jua, jub) need no element mask for any row (the others are computed with it)
   int jlo, jhi, jua, jub;
   int lo_key, hi_key;   // keys this lane's row sees: lo_key <= key <= hi_key
+  int w_lo, w_hi;       // keys some row of this wave sees (w_lo > w_hi: none), wave-uniform
   float sl2;
   V8 qf[C::NS];
   f32x16 oacc[C::NCB];
@@ -139,6 +140,11 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
     const int last_wg = min(q0 + C::BR, sq.nq) - 1;
     lo_key = has_l ? qrow + diag - a.wl : -0x7fffffff;
     hi_key = min(nk, has_r ? qrow + diag + a.wr + 1 : nk) - 1;
+    // the wave's first row has the smallest bounds, its last valid row the largest
+    const int w_last = min(q0w + 31, sq.nq - 1);
+    w_lo = has_l ? max(0, q0w + diag - a.wl) : 0;
+    w_hi = min(nk, has_r ? w_last + diag + a.wr + 1 : nk) - 1;
+    if (w_last < q0w) w_hi = -1;   // the wave has no rows
     // tiles of the workgroup
     const int kb = lbound(q0), ke = rbound(last_wg);
     jlo = kb / C::BC;
@@ -387,16 +393,19 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
       pv(lds.v[ST], pf);
       if (BF16) l_part += rounded_sum(pf);
     } else {
-      // masked tiles: every wave computes them with the element mask, so the
-      // step stays straight-line code (a wave that sees none of the tile gets
-      // probabilities 0 from it)
-      SA sacc;
-      PF pf;
-      qk(lds.k[ST], sacc);
-      rebase(rowmax<true>(sacc, j));
-      add_sum(probs<true>(sacc, pf));
-      pv(lds.v[ST], pf);
-      if (BF16) l_part += rounded_sum(pf);
+      // masked tiles (diagonal, band edges, key tail) with the element mask; a
+      // wave none of whose rows sees a key of the tile skips the products (all
+      // its probabilities would be 0) but still takes part in the DMA and
+      // barrier. Not for d > 128, where the branch would make the kernel spill.
+      if (D > 128 || (j * C::BC <= w_hi && (j + 1) * C::BC - 1 >= w_lo && w_lo <= w_hi)) {
+        SA sacc;
+        PF pf;
+        qk(lds.k[ST], sacc);
+        rebase(rowmax<true>(sacc, j));
+        add_sum(probs<true>(sacc, pf));
+        pv(lds.v[ST], pf);
+        if (BF16) l_part += rounded_sum(pf);
+      }
     }
     __syncthreads();
   }
