@@ -17,7 +17,7 @@
 //
 // Per loop step j: issue the DMA of tile j+1 into the stage freed by step
 // j-1; S_j = K_j Q^T on MFMA; softmax; O += V_j P_j on MFMA; barrier. Each
-// tile's loads have a whole step to land. For d <= 128 the kernel fits in 256
+// tile's loads have a whole step to land. For d <= 192 the kernel fits in 256
 // registers, so two workgroups (three at d = 64, four at d = 32) share a CU and
 // each SIMD can interleave one wave's exponentials with another wave's matrix
 // products.
@@ -37,12 +37,12 @@
 namespace fa {
 
 template <int D> struct FwdCfg {
-  // four waves, one per SIMD; for d <= 128 the kernel fits 256 registers so two
+  // four waves, one per SIMD; for d <= 192 the kernel fits 256 registers so two
   // or more workgroups share a CU (several waves per SIMD, each with its own barrier)
-  // waves per SIMD: small head dims have little MFMA work per score, so more
-  // waves per SIMD overlap one's softmax with another's products (registers
-  // allow four at d = 32 and three at d = 64 without spills)
-  static constexpr int WPE = (D <= 32) ? 4 : (D <= 64) ? 3 : (D <= 128) ? 2 : 1;
+  // waves per SIMD: a second (third, fourth) wave overlaps one wave's softmax
+  // with another's products; registers allow four at d = 32, three at d = 64 and
+  // two up to d = 192 without spills (d = 256 would spill at two)
+  static constexpr int WPE = (D <= 32) ? 4 : (D <= 64) ? 3 : (D <= 192) ? 2 : 1;
   static constexpr int NW = 4;                       // waves per workgroup
   static constexpr int THREADS = NW * 64;
   static constexpr int BR = 32 * NW;                 // query rows per workgroup
