@@ -17,10 +17,10 @@
 //
 // Per loop step j: issue the DMA of tile j+1 into the stage freed by step
 // j-1; S_j = K_j Q^T on MFMA; softmax; O += V_j P_j on MFMA; barrier. Each
-// tile's loads have a whole step to land. For d <= 192 the kernel fits in 256
-// registers, so two workgroups (three at d = 64, four at d = 32) share a CU and
-// each SIMD can interleave one wave's exponentials with another wave's matrix
-// products.
+// tile's loads have a whole step to land. The kernel is held to 256 registers
+// (a few spilled at d = 256), so two workgroups (three at d = 64, four at
+// d = 32) share a CU and each SIMD can interleave one wave's exponentials with
+// another wave's matrix products.
 //
 // The reference max m used in P = exp2(s * scale * log2(e) - m) need not be
 // the running max: O and the row sum share it, so the result is the same for
@@ -37,12 +37,12 @@
 namespace fa {
 
 template <int D> struct FwdCfg {
-  // four waves, one per SIMD; for d <= 192 the kernel fits 256 registers so two
-  // or more workgroups share a CU (several waves per SIMD, each with its own barrier)
-  // waves per SIMD: a second (third, fourth) wave overlaps one wave's softmax
-  // with another's products; registers allow four at d = 32, three at d = 64 and
-  // two up to d = 192 without spills (d = 256 would spill at two)
-  static constexpr int WPE = (D <= 32) ? 4 : (D <= 64) ? 3 : (D <= 192) ? 2 : 1;
+  // four waves, one per SIMD, and two or more workgroups per CU (several waves
+  // per SIMD, each workgroup with its own barrier): a second (third, fourth) wave
+  // overlaps one wave's softmax with another's products. Registers allow four
+  // at d = 32, three at d = 64 and two up to d = 192 without spills; d = 256 at
+  // two spills a few dozen bytes per lane and is still much faster than at one.
+  static constexpr int WPE = (D <= 32) ? 4 : (D <= 64) ? 3 : 2;
   static constexpr int NW = 4;                       // waves per workgroup
   static constexpr int THREADS = NW * 64;
   static constexpr int BR = 32 * NW;                 // query rows per workgroup
@@ -109,7 +109,11 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
   int64_t valid;
   uint32_t goff[C::NDMA];
   // LDS read offsets of this lane's fragments: K slice s, V^T c-block cb (low and high 4 keys)
+  // (d = 256: recomputed per read from the bases below instead; the 32 registers
+  // they would take are what two waves per SIMD need)
+  static constexpr bool kPreOfs = D <= 192;
   uint32_t kofs[C::NS], vlo[C::NCB], vhi[C::NCB];
+  uint32_t kro, kxo, vb0, vb1, vx0, vx1;
 
   // first key row i sees, and one past its last (band and cache bounds)
   __device__ __forceinline__ int lbound(int i) const {
@@ -174,16 +178,16 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
     // LDS read offsets (the swizzle only sees the low 4 row bits), computed once:
     // one register each saves an ALU op per fragment read in the loop
     // K: row 32kb + ln32, chunk (2s | hh) ^ swz(ln32) -> byte (kxo ^ 32s) + row offset
-    const uint32_t kro = ln32 * (D * 2);
-    const uint32_t kxo = (static_cast<uint32_t>(hh) ^ Swz<D>::f(ln32)) << 4;
+    kro = ln32 * (D * 2);
+    kxo = (static_cast<uint32_t>(hh) ^ Swz<D>::f(ln32)) << 4;
     // V: rows 16t + vrow0 (+8), chunk (4cb + vxl) ^ swz(row) -> byte (vx ^ 64cb) + row offset
     const uint32_t vj = lane & 15, vcb = (lane >> 4) & 1;
     const uint32_t vrow0 = 4 * hh + (vj >> 2), vrow1 = vrow0 + 8;
     const uint32_t vxl = 2 * vcb + ((vj & 3) >> 1);
-    const uint32_t vx0 = (vxl ^ Swz<D>::f(vrow0)) << 4;
-    const uint32_t vx1 = (vxl ^ Swz<D>::f(vrow1)) << 4;
-    const uint32_t vb0 = vrow0 * (D * 2) + 8 * (vj & 1);
-    const uint32_t vb1 = vrow1 * (D * 2) + 8 * (vj & 1);
+    vx0 = (vxl ^ Swz<D>::f(vrow0)) << 4;
+    vx1 = (vxl ^ Swz<D>::f(vrow1)) << 4;
+    vb0 = vrow0 * (D * 2) + 8 * (vj & 1);
+    vb1 = vrow1 * (D * 2) + 8 * (vj & 1);
 #pragma unroll
     for (int i = 0; i < C::NS; ++i) kofs[i] = (kxo ^ (32u * i)) + kro;
 #pragma unroll
@@ -227,12 +231,12 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
 
   // LDS fragments: K (A operand of S^T) and V^T (A operand of O^T) at precomputed offsets
   __device__ __forceinline__ V8 kfrag(const char* kt, int kb, int s) const {
-    const uint32_t off = kb * 32 * (D * 2) + kofs[s];
+    const uint32_t off = kb * 32 * (D * 2) + (kPreOfs ? kofs[s] : (kxo ^ (32u * s)) + kro);
     return lds_read_v8<V8>(kt, off);
   }
   __device__ __forceinline__ V8 vfrag(const char* vt, int cb, int t) const {
-    const uint32_t lo = t * 16 * (D * 2) + vlo[cb];
-    const uint32_t hi = t * 16 * (D * 2) + vhi[cb];
+    const uint32_t lo = t * 16 * (D * 2) + (kPreOfs ? vlo[cb] : (vx0 ^ (64u * cb)) + vb0);
+    const uint32_t hi = t * 16 * (D * 2) + (kPreOfs ? vhi[cb] : (vx1 ^ (64u * cb)) + vb1);
     return __builtin_bit_cast(V8, __builtin_shufflevector(lds_read_tr(vt, lo), lds_read_tr(vt, hi),
                                                           0, 1, 2, 3, 4, 5, 6, 7));
   }
@@ -373,6 +377,7 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
   // the O accumulators keep their registers across the loop.
   template <int ST, bool TAIL>
   __device__ __forceinline__ void step(int j, const FwdLds<D>& lds) {
+    if (!kPreOfs) asm volatile("" : "+v"(kxo), "+v"(vx0), "+v"(vx1));
     if (j + 1 < jhi) {
       dma(kg, j + 1, lds.k[ST ^ 1]);
       dma(vg, j + 1, lds.v[ST ^ 1]);
