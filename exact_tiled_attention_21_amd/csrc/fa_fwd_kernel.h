@@ -36,17 +36,20 @@
 
 namespace fa {
 
-template <int D> struct FwdCfg {
+template <int D, bool BAND> struct FwdCfg {
   // four waves, one per SIMD, and two or more workgroups per CU (several waves
   // per SIMD, each workgroup with its own barrier): a second (third, fourth) wave
   // overlaps one wave's softmax with another's products. Registers allow four
   // at d = 32, three at d = 64 and two up to d = 192 without spills; d = 256 at
   // two spills a few dozen bytes per lane and is still much faster than at one.
-  static constexpr int WPE = (D <= 32) ? 4 : (D <= 64) ? 3 : 2;
+  // d = 128 without a band takes 32-key tiles, which free the registers (and
+  // LDS) for a third wave; the banded kernel would spill with them.
+  static constexpr bool kNarrow = D == 128 && !BAND;
+  static constexpr int WPE = (D <= 32) ? 4 : (D <= 64 || kNarrow) ? 3 : 2;
   static constexpr int NW = 4;                       // waves per workgroup
   static constexpr int THREADS = NW * 64;
   static constexpr int BR = 32 * NW;                 // query rows per workgroup
-  static constexpr int BC = (D <= 128) ? 64 : 32;    // keys per LDS tile
+  static constexpr int BC = (D <= 128 && !kNarrow) ? 64 : 32;    // keys per LDS tile
   static constexpr int KB = BC / 32;                 // 32-key blocks of S^T
   static constexpr int NS = D / 16;                  // 16-wide d slices (QK^T depth)
   static constexpr int NCB = D / 32;                 // 32-wide d blocks of O^T
@@ -72,15 +75,15 @@ struct FwdSeq {
 
 // LDS of one workgroup: two stages each for K and V, as separate objects so the
 // compiler knows a DMA into one stage never feeds a read of the other.
-template <int D> struct FwdLds {
-  static constexpr int TB = FwdCfg<D>::TILE_BYTES;
+template <int D, bool BAND> struct FwdLds {
+  static constexpr int TB = FwdCfg<D, BAND>::TILE_BYTES;
   char* k[2];
   char* v[2];
 };
 
 // Per-wave state and the steps of the tile loop (device code only).
 template <int D, bool BF16, bool BAND> struct FwdWave {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, BAND>;
   using E = Elem<BF16>;
   using T = typename E::T;
   using V8 = typename E::V8;
@@ -376,7 +379,7 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
   // diagonal) or has no visible key; the other steps are straight-line code so
   // the O accumulators keep their registers across the loop.
   template <int ST, bool TAIL>
-  __device__ __forceinline__ void step(int j, const FwdLds<D>& lds) {
+  __device__ __forceinline__ void step(int j, const FwdLds<D, BAND>& lds) {
     if (!kPreOfs) asm volatile("" : "+v"(kxo), "+v"(vx0), "+v"(vx1));
     if (j + 1 < jhi) {
       dma(kg, j + 1, lds.k[ST ^ 1]);
@@ -420,7 +423,7 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
   // directly writes 16 scattered bytes per row and instruction; instead the
   // wave's 32 x D tile of O goes through its own slice of the (now idle) K/V
   // LDS stages, and each 16-byte store instruction then writes whole rows.
-  __device__ __forceinline__ void finish(int hq, const FwdLds<D>& lds) {
+  __device__ __forceinline__ void finish(int hq, const FwdLds<D, BAND>& lds) {
     const float l = halves_sum(l_part);
     const float l_lse = BF16 ? halves_sum(l_exact) : l;
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -460,9 +463,9 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
 };
 
 template <int D, bool BF16, bool BAND>
-__global__ __launch_bounds__(FwdCfg<D>::THREADS)
-__attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fa_fwd_kernel(const FwdArgs a) {
-  using C = FwdCfg<D>;
+__global__ __launch_bounds__((FwdCfg<D, BAND>::THREADS))
+__attribute__((amdgpu_waves_per_eu((FwdCfg<D, BAND>::WPE), (FwdCfg<D, BAND>::WPE)))) void fa_fwd_kernel(const FwdArgs a) {
+  using C = FwdCfg<D, BAND>;
   __shared__ __attribute__((aligned(1024))) char k_lds0[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char k_lds1[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v_lds0[C::TILE_BYTES];
@@ -502,7 +505,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fa_fwd
   }
 
   FwdWave<D, BF16, BAND> w(a, sq, hq, g, qt);
-  const FwdLds<D> lds{{k_lds0, k_lds1}, {v_lds0, v_lds1}};
+  const FwdLds<D, BAND> lds{{k_lds0, k_lds1}, {v_lds0, v_lds1}};
   // tile j lives in stage (j - jlo) & 1; the first tile's DMA goes out before
   // the Q loads, so the prologue waits for one memory latency, not two
   if (w.jhi > w.jlo) {
@@ -547,7 +550,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fa_fwd
 
 template <int D>
 hipError_t launch_fwd_d(const FwdArgs& a, bool bf16, bool band, hipStream_t stream) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, false>;   // threads per workgroup: the same with and without a band
+  static_assert(C::THREADS == FwdCfg<D, true>::THREADS, "one block size");
   const dim3 grid(static_cast<unsigned>(a.n_qtiles) * a.Hq * a.B);
   const dim3 block(C::THREADS);
   (void)hipGetLastError();   // start from a clean error state
