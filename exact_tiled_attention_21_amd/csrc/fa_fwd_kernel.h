@@ -18,9 +18,9 @@
 // Per loop step j: issue the DMA of tile j+1 into the stage freed by step
 // j-1; S_j = K_j Q^T on MFMA; softmax; O += V_j P_j on MFMA; barrier. Each
 // tile's loads have a whole step to land. The kernel is held to 256 registers
-// (a few spilled at d = 256), so two workgroups (three at d = 64, four at
-// d = 32) share a CU and each SIMD can interleave one wave's exponentials with
-// another wave's matrix products.
+// or fewer (a few spilled at d = 256), so two workgroups (four at d = 32,
+// three at d = 64 and at d = 128 without a band) share a CU and each SIMD can
+// interleave one wave's exponentials with another wave's matrix products.
 //
 // The reference max m used in P = exp2(s * scale * log2(e) - m) need not be
 // the running max: O and the row sum share it, so the result is the same for
