@@ -34,11 +34,26 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_headline_traffic.json")
 KERNEL_SOURCES = ("fa_fwd_kernel.h", "fa_device.h", "fa_launch.h")
 
 
-def kernel_source_hash() -> str:
+def code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed: a comment edit
+    leaves the kernel, and so its hash, unchanged."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_hash(read=None) -> str:
+    """Hash of the forward kernel's code (comments and layout ignored)."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "exact_tiled_attention_21_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        path = os.path.join("exact_tiled_attention_21_amd", "csrc", f)
+        if read is None:
+            with open(os.path.join(ROOT, path), encoding="utf-8") as fh:
+                text = fh.read()
+        else:
+            text = read(path)
+        h.update(code_only(text).encode())
     return h.hexdigest()[:16]
 
 
