@@ -19,7 +19,7 @@
 // j-1; S_j = K_j Q^T on MFMA; softmax; O += V_j P_j on MFMA; barrier. Each
 // tile's loads have a whole step to land. The kernel is held to 256 registers
 // or fewer (a few spilled at d = 256), so two workgroups (four at d = 32,
-// three at d = 64 and d = 128) share a CU and each SIMD can interleave one
+// three at d = 64, 96 and 128) share a CU and each SIMD can interleave one
 // wave's exponentials with another wave's matrix products.
 //
 // The reference max m used in P = exp2(s * scale * log2(e) - m) need not be
@@ -42,10 +42,10 @@ template <int D, bool BAND> struct FwdCfg {
   // overlaps one wave's softmax with another's products. Registers allow four
   // at d = 32, three at d = 64 and two up to d = 192 without spills; d = 256 at
   // two spills a few dozen bytes per lane and is still much faster than at one.
-  // d = 128 takes 32-key tiles, which free the registers (and LDS) for a third
-  // wave (with a band only without the per-wave skip of masked tiles, which
-  // would make it spill).
-  static constexpr bool kNarrow = D == 128;
+  // d = 96 and 128 take 32-key tiles, which free the registers (and LDS) for a
+  // third wave (with a band only without the per-wave skip of masked tiles,
+  // which would make it spill).
+  static constexpr bool kNarrow = D == 96 || D == 128;
   static constexpr int WPE = (D <= 32) ? 4 : (D <= 64 || kNarrow) ? 3 : 2;
   static constexpr int NW = 4;                       // waves per workgroup
   static constexpr int THREADS = NW * 64;
@@ -405,9 +405,9 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
       // masked tiles (diagonal, band edges, key tail) with the element mask; a
       // wave none of whose rows sees a key of the tile skips the products (all
       // its probabilities would be 0) but still takes part in the DMA and
-      // barrier. Only below d = 128: the branch costs ~45 registers, which at
-      // d = 128 would block the third wave and beyond would spill.
-      if (D >= 128 || (j * C::BC <= w_hi && (j + 1) * C::BC - 1 >= w_lo && w_lo <= w_hi)) {
+      // barrier. Only below d = 96: the branch costs ~45 registers, which at
+      // d = 96 and 128 would block the third wave and beyond would spill.
+      if (D >= 96 || (j * C::BC <= w_hi && (j + 1) * C::BC - 1 >= w_lo && w_lo <= w_hi)) {
         SA sacc;
         PF pf;
         qk(lds.k[ST], sacc);
