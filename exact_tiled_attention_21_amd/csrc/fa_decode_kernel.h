@@ -29,11 +29,12 @@
 // table maps each sequence's logical key blocks to pages of a shared pool, and
 // cache_seqlens gives each sequence's length): a 32-key tile never straddles a
 // page (the page size is a multiple of 32), so each tile costs one block-table
-// read and otherwise loads exactly like a contiguous tile. Chunks are cut per
-// sequence from its own length, and the causal mask is aligned to it.
+// read and otherwise loads exactly like a contiguous tile. The tiles dealt out
+// are those below each sequence's own length, and the causal mask is aligned
+// to it.
 //
 // Combine kernel: per output row, LSE = log sum_s exp(LSE_s) and
-// O = sum_s exp(LSE_s - LSE) O_s; chunks with LSE_s = -inf weigh nothing.
+// O = sum_s exp(LSE_s - LSE) O_s; parts with LSE_s = -inf weigh nothing.
 #pragma once
 
 #include "fa_device.h"
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(const DecodeArgs
 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, bool bf16, bool causal, hipStream_t stream) {
-  const dim3 grid1(a.Hkv * a.row_blocks, a.splits, a.B);   // splits = sub-chunks of all chunks
+  const dim3 grid1(a.Hkv * a.row_blocks, a.splits, a.B);   // a.splits = all parts
   (void)hipGetLastError();   // start from a clean error state
   const bool paged = a.block_table != nullptr;
 #define FA_DEC_SPLIT(BF, CA)                                                     \

@@ -39,8 +39,8 @@ struct DecodeArgs {
   float* part_lse; // [S][B][Hq][Nq] float32, log2 domain
   int B, Nq, Nk, Hq, Hkv;
   int group;       // Hq / Hkv
-  int splits;      // partials per row: sub_per sub-chunks per requested chunk
-  int sub_per;     // sub-chunks per chunk: 1, 2 or 4
+  int splits;      // parts (partials per row): sub_per parts per requested split
+  int sub_per;     // parts per requested split: 1, 2 or 4
   int row_blocks;  // ceil(group * Nq / 32)
   float sl2;       // scale * log2(e)
   // paged cache (block_table non-null): k and v point at page pools
