@@ -413,9 +413,7 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
     // with a causal band the first key tiles see the most query rows
     blocked_order(blockIdx.x, nkt, a.Hkv * a.B, a.hb_kv, kt, gb);
   } else {
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    kt = bid % nkt;
-    gb = bid / nkt;
+    xcd_heads(blockIdx.x, nkt, a.Hkv * a.B, gridDim.x, kt, gb);
   }
   const int g = gb % a.Hkv;
   const int b = gb / a.Hkv;
@@ -618,9 +616,7 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
     blocked_order(blockIdx.x, nqt, a.Hq * a.B, a.hb_q, o, hb);
     qt = nqt - 1 - o;
   } else {
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    qt = bid % nqt;
-    hb = bid / nqt;
+    xcd_heads(blockIdx.x, nqt, a.Hq * a.B, gridDim.x, qt, hb);
   }
   const int hq = hb % a.Hq;
   const int b = hb / a.Hq;

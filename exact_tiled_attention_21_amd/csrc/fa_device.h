@@ -165,6 +165,26 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return (bid & 7) * per + (bid >> 3);
 }
 
+// Work order without a band: the (batch, head) pairs are dealt out round-robin
+// over the 8 XCDs (pair p runs on XCD p mod 8, since workgroup ids go to the
+// XCDs round-robin) and each pair's tiles stay on its XCD, where they share the
+// pair's K/V in L2. Every XCD gets every eighth pair, so packed sequences of
+// unequal length still spread evenly over the XCDs (contiguous ranges of pairs
+// per XCD gave one XCD 1.7x the mean work on a 16-sequence batch). Falls back
+// to contiguous ranges when the pair count is not a multiple of 8.
+__device__ __forceinline__ void xcd_heads(int bid, int ntiles, int nheads, int n, int& tile, int& head) {
+  if ((nheads & 7) == 0) {
+    const int m = bid >> 3;
+    const int hl = m / ntiles;
+    tile = m - hl * ntiles;
+    head = hl * 8 + (bid & 7);
+  } else {
+    const int r = xcd_remap(bid, n);
+    tile = r % ntiles;
+    head = r / ntiles;
+  }
+}
+
 // Work order for masks that make tile workloads uneven (causal). Workgroup ids
 // go to the heads in blocks of hb heads (the host sizes a block so that its
 // operands stay resident in the last-level cache); inside a block the tiles

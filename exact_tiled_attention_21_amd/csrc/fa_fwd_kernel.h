@@ -481,9 +481,7 @@ __attribute__((amdgpu_waves_per_eu((FwdCfg<D, BAND>::WPE), (FwdCfg<D, BAND>::WPE
     blocked_order(blockIdx.x, a.n_qtiles, a.Hq * a.B, a.hb, o, hb);
     qt = a.n_qtiles - 1 - o;
   } else {
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    qt = bid % a.n_qtiles;
-    hb = bid / a.n_qtiles;
+    xcd_heads(blockIdx.x, a.n_qtiles, a.Hq * a.B, gridDim.x, qt, hb);
   }
   const int hq = hb % a.Hq;
   const int b = hb / a.Hq;
