@@ -613,10 +613,10 @@ void fa_bwd_dq_kernel(const BwdArgs a) {
   if (BAND) {
     // with a causal band the last query tiles see the most keys
     int o;
-    blocked_order(blockIdx.x, nqt, a.Hq * a.B, a.hb_q, o, hb);
+    blocked_order(blockIdx.x, nqt, a.Hq * a.B, a.hb_q, o, hb, a.group);
     qt = nqt - 1 - o;
   } else {
-    xcd_heads(blockIdx.x, nqt, a.Hq * a.B, gridDim.x, qt, hb);
+    xcd_heads(blockIdx.x, nqt, a.Hq * a.B, gridDim.x, qt, hb, a.group);
   }
   const int hq = hb % a.Hq;
   const int b = hb / a.Hq;

@@ -171,13 +171,18 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 // pair's K/V in L2. Every XCD gets every eighth pair, so packed sequences of
 // unequal length still spread evenly over the XCDs (contiguous ranges of pairs
 // per XCD gave one XCD 1.7x the mean work on a 16-sequence batch). Falls back
-// to contiguous ranges when the pair count is not a multiple of 8.
-__device__ __forceinline__ void xcd_heads(int bid, int ntiles, int nheads, int n, int& tile, int& head) {
+// to contiguous ranges when the pair count is not a multiple of 8. With
+// grouped-query heads (`group` consecutive query heads per KV head) the pairs
+// of one KV head all go to the same XCD, where they share its K/V.
+__device__ __forceinline__ void xcd_heads(int bid, int ntiles, int nheads, int n, int& tile, int& head,
+                                          int group = 1) {
   if ((nheads & 7) == 0) {
     const int m = bid >> 3;
     const int hl = m / ntiles;
     tile = m - hl * ntiles;
-    head = hl * 8 + (bid & 7);
+    const int x = bid & 7;
+    head = (group > 1 && nheads % (8 * group) == 0) ? (x + 8 * (hl / group)) * group + hl % group
+                                                   : hl * 8 + x;
   } else {
     const int r = xcd_remap(bid, n);
     tile = r % ntiles;
@@ -191,13 +196,23 @@ __device__ __forceinline__ void xcd_heads(int bid, int ntiles, int nheads, int n
 // come heaviest first, with the head varying fastest, so the ids on one XCD
 // (id mod 8) keep revisiting the same heads and the machine drains on light
 // tiles. `order` 0 is the heaviest tile; the caller maps it to a tile index.
-__device__ __forceinline__ void blocked_order(int p, int ntiles, int nheads, int hb, int& order, int& head) {
+// With grouped-query heads (`group` query heads per KV head, consecutive), the
+// heads inside a block are permuted so that all query heads of one KV head
+// land on the same XCD and share its K/V in that XCD's L2 (when the block size
+// is a multiple of 8 groups; otherwise the plain order).
+__device__ __forceinline__ void blocked_order(int p, int ntiles, int nheads, int hb, int& order, int& head,
+                                              int group = 1) {
   const int per_block = hb * ntiles;
   const int blk = p / per_block;
   const int r = p - blk * per_block;
   const int cnt = min(hb, nheads - blk * hb);
   order = r / cnt;
-  head = blk * hb + (r - order * cnt);
+  int hi = r - order * cnt;   // slot in the block: XCD = hi mod 8
+  if (group > 1 && hb % group == 0 && cnt % (8 * group) == 0) {
+    const int x = hi & 7, t = hi >> 3;
+    hi = (x + 8 * (t / group)) * group + t % group;
+  }
+  head = blk * hb + hi;
 }
 
 }  // namespace fa

@@ -478,10 +478,10 @@ __attribute__((amdgpu_waves_per_eu((FwdCfg<D, BAND>::WPE), (FwdCfg<D, BAND>::WPE
   if (BAND) {
     // with a causal band the last query tiles see the most keys
     int o;
-    blocked_order(blockIdx.x, a.n_qtiles, a.Hq * a.B, a.hb, o, hb);
+    blocked_order(blockIdx.x, a.n_qtiles, a.Hq * a.B, a.hb, o, hb, a.group);
     qt = a.n_qtiles - 1 - o;
   } else {
-    xcd_heads(blockIdx.x, a.n_qtiles, a.Hq * a.B, gridDim.x, qt, hb);
+    xcd_heads(blockIdx.x, a.n_qtiles, a.Hq * a.B, gridDim.x, qt, hb, a.group);
   }
   const int hq = hb % a.Hq;
   const int b = hb / a.Hq;
