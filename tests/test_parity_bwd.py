@@ -88,6 +88,15 @@ def test_head_dims(d, dtype, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_grouped_heads_order(causal, d):
+    """32 (batch, head) pairs with 4 query heads per KV head: the work orders keep
+    a KV group's query heads on one XCD (a permutation used only when the pair
+    count is a multiple of 8 groups), in the dQ pass as in the forward."""
+    run_full(97, 2, 300, 300, 16, 4, d, "bf16", causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_oracle_forward_inputs(causal):
     """O and LSE from the oracle: the backward kernels checked on their own."""
     run_full(650 + int(causal), 2, 257, 300, 4, 2, 128, "bf16", causal, fwd="oracle")

@@ -100,6 +100,16 @@ def test_reference_moves_in_unmasked_tiles(dtype, causal):
     cmp.check_lse(to_np(lse), lse_ref, what)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_grouped_heads_order(causal, dtype, d):
+    """32 (batch, head) pairs with 4 query heads per KV head and a ragged query
+    count: the work orders keep a KV group's query heads on one XCD (a permutation
+    used only when the pair count is a multiple of 8 groups)."""
+    run_full(96, 2, 300, 300, 16, 4, d, dtype, causal)
+
+
 def test_scale_is_used_as_passed():
     run_full(300, 1, 130, 130, 2, 2, 64, "f16", False, scale=0.37)
     run_full(301, 1, 130, 130, 2, 2, 64, "bf16", True, scale=0.0)
