@@ -103,8 +103,8 @@ fa_status launch_decode_common(fa::DecodeArgs& a, const void* q, void* o, float*
                                fa_dtype dtype, void* workspace, void* stream) {
   const int group = Hq / Hkv;
   const int64_t row_blocks = (int64_t(group) * Nq + 31) / 32;
-  if (int64_t(kSubPerChunk) * num_splits > 65535 || B > 65535) return FA_ERR_SHAPE;  // grid y / z limits
-  if (row_blocks * Hkv > 0x7fffffffLL) return FA_ERR_SHAPE;
+  // split grid: x = batch, y = parts, z = KV heads x row blocks (y and z at most 65535)
+  if (int64_t(kSubPerChunk) * num_splits > 65535 || row_blocks * Hkv > 65535) return FA_ERR_SHAPE;
   a.q = q; a.o = o; a.lse = lse;
   const size_t rows = size_t(kSubPerChunk) * num_splits * B * Hq * Nq;
   a.part_o = static_cast<float*>(workspace);

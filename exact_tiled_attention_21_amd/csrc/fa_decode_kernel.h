@@ -257,12 +257,14 @@ __global__ __launch_bounds__(64) void fa_decode_split_kernel(const DecodeArgs a)
   __shared__ __attribute__((aligned(1024))) char kt[C::TILE];
   __shared__ __attribute__((aligned(1024))) char vt[C::TILE];
 
-  // the KV heads of one key range are consecutive in dispatch order: their rows
-  // interleave in memory, so reading them together keeps DRAM pages open
+  // the batch index is the grid's fastest axis, so the workgroups of one
+  // sequence share an XCD (workgroup ids go to the XCDs round-robin): the KV
+  // heads of a cache row, which interleave in memory, are then all read from
+  // one XCD (with a single sequence, the heads of one part are)
   const int part = blockIdx.y;            // one of the a.splits parts
-  const int g = blockIdx.x % a.Hkv;
-  const int rb = blockIdx.x / a.Hkv;
-  const int b = blockIdx.z;
+  const int g = blockIdx.z % a.Hkv;
+  const int rb = blockIdx.z / a.Hkv;
+  const int b = blockIdx.x;
   W w(a, part, g, rb, b);
 
   // tiles t of this part: the loads of tile t + 1 are issued once tile t sits in
@@ -359,7 +361,7 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(const DecodeArgs
 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, bool bf16, bool causal, hipStream_t stream) {
-  const dim3 grid1(a.Hkv * a.row_blocks, a.splits, a.B);   // a.splits = all parts
+  const dim3 grid1(a.B, a.splits, a.Hkv * a.row_blocks);   // a.splits = all parts
   (void)hipGetLastError();   // start from a clean error state
   const bool paged = a.block_table != nullptr;
 #define FA_DEC_SPLIT(BF, CA)                                                     \

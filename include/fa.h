@@ -148,7 +148,8 @@ size_t fa_decode_workspace_bytes(int B, int Nq, int Hq, int d, int num_splits);
  *                neighbouring tiles at the same time). Parts with no tile are
  *                empty and weigh nothing. The merged result does not depend on
  *                the partition beyond float32 rounding.
- *                Nk * Hkv * d * 2 must stay below 2^31 (FA_ERR_SHAPE).
+ *                Nk * Hkv * d * 2 must stay below 2^31, and Hkv times
+ *                ceil(Hq / Hkv * Nq / 32) at most 65535 (FA_ERR_SHAPE).
  *   causal     : as in fa_fwd (bottom-right aligned against Nk).
  *   workspace  : caller-owned device buffer of at least
  *                fa_decode_workspace_bytes(B, Nq, Hq, d, num_splits) bytes,
