@@ -311,8 +311,12 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(const DecodeArgs
   constexpr int RPB = 256 / TPR;
   constexpr int SB = 16;
   const int rows = a.B * a.Hq * a.Nq;
-  const int row = blockIdx.x * RPB + threadIdx.x / TPR;
-  if (row >= rows) return;
+  // the batch varies fastest over the workgroups, like in the split kernel, so
+  // batch b's partials are merged on the XCD that wrote them
+  const int rows_b = a.Hq * a.Nq;
+  const int rloc = (blockIdx.x / a.B) * RPB + threadIdx.x / TPR;
+  if (rloc >= rows_b) return;
+  const int row = (blockIdx.x % a.B) * rows_b + rloc;
   const int c4 = (threadIdx.x % TPR) * 4;
   const size_t stride = static_cast<size_t>(rows);   // elements between parts
   float mx = kNegInf;
@@ -380,8 +384,7 @@ hipError_t launch_decode_d(const DecodeArgs& a, bool bf16, bool causal, hipStrea
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int RPB = 256 / (D / 4);
-  const int rows = a.B * a.Hq * a.Nq;
-  const dim3 grid2((rows + RPB - 1) / RPB);
+  const dim3 grid2(static_cast<unsigned>(a.B) * ((a.Hq * a.Nq + RPB - 1) / RPB));
   if (bf16) fa_decode_combine_kernel<D, true><<<grid2, 256, 0, stream>>>(a);
   else fa_decode_combine_kernel<D, false><<<grid2, 256, 0, stream>>>(a);
   return hipGetLastError();
