@@ -74,6 +74,17 @@ def test_many_rows_per_group():
     run(801, 1, 40, 600, 4, 4, 64, "bf16", 4, causal=True)
 
 
+@pytest.mark.parametrize("case", [(5, 3, 6, 2, 96, "bf16", False), (3, 12, 8, 2, 64, "f16", False),
+                                  (7, 12, 8, 2, 96, "bf16", True), (13, 1, 32, 8, 128, "bf16", False)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_odd_batch_and_row_blocks(case):
+    """Batch counts that are not a multiple of the 8 XCDs (the batch is the
+    split grid's fastest axis and the combine's), two 32-row blocks per KV head,
+    and per-batch row counts that leave the combine's last workgroup partly idle."""
+    B, Nq, Hq, Hkv, d, dtype, causal = case
+    run(950 + B + Nq, B, Nq, 900, Hq, Hkv, d, dtype, 8, causal=causal)
+
+
 def test_decode_matches_forward():
     wid, B, Nq, Nk, Hq, Hkv, d = 900, 2, 8, 4096, 32, 8, 128
     qb, kb, vb = inputs(wid, B, Nq, Nk, Hq, Hkv, d, "bf16")
