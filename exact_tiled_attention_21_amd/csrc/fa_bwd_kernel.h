@@ -140,14 +140,18 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const BwdArgs a) {
   constexpr int RPB = 256 / G;
   const int nqp = bwd_nq_pad(a.Nq);
   const int64_t entries = static_cast<int64_t>(a.B) * a.Hq * nqp;
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / G;
+  // thread groups enumerate (b, i, h) with the head fastest, so consecutive
+  // groups read adjacent 16-byte chunks of the same [Hq][d] row of O and dO;
+  // the statistics go to entry (b h) nqp + i
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / G;
   const int c = threadIdx.x % G;
-  const int i = static_cast<int>(e % nqp);
-  const int64_t bh = e / nqp;
-  const int h = static_cast<int>(bh % a.Hq);
-  const int b = static_cast<int>(bh / a.Hq);
-  const BwdSeq sq(a, e < entries ? b : 0);
-  const bool live = e < entries && i < sq.nq;
+  const int h = static_cast<int>(t % a.Hq);
+  const int64_t bi = t / a.Hq;
+  const int i = static_cast<int>(bi % nqp);
+  const int b = static_cast<int>(bi / nqp);
+  const int64_t e = (static_cast<int64_t>(b) * a.Hq + h) * nqp + i;
+  const BwdSeq sq(a, t < entries ? b : 0);
+  const bool live = t < entries && i < sq.nq;
   float acc = 0.f;
   if (live && c < CPR) {
     const int64_t row = ((static_cast<int64_t>(sq.q_row0) + i) * a.Hq + h) * D + 8 * c;
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const BwdArgs a) {
   }
 #pragma unroll
   for (int m = G / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, G);
-  if (e < entries && c == 0) {
+  if (t < entries && c == 0) {
     float l2 = __builtin_huge_valf();
     if (live) {
       const float l = a.lse[sq.lse_index(a, b, h, i)];
