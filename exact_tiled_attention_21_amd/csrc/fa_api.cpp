@@ -66,6 +66,10 @@ hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool band, hipStream_t
 namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;  // per tensor, keeps 64-bit offsets far from overflow
+// Hq * d at most 2^22 elements: the kernels address a tile of up to 64 rows
+// from its first row with 32-bit byte offsets (row x heads x d x 2 bytes), so
+// one row of all heads must stay below 2^31 / 64 bytes.
+constexpr int64_t kMaxRowElems = int64_t(1) << 22;
 
 bool head_dim_ok(int d) {
   return d == 32 || d == 64 || d == 96 || d == 128 || d == 192 || d == 256;
@@ -83,6 +87,7 @@ fa_status check_common(const void* q, const void* k, const void* v, void* o, con
   if (!isfinite(scale)) return FA_ERR_SCALE;
   const int64_t qe = int64_t(B) * Nq * Hq * d, ke = int64_t(B) * Nk * Hkv * d;
   if (qe > kMaxElems || ke > kMaxElems) return FA_ERR_SHAPE;
+  if (int64_t(Hq) * d > kMaxRowElems) return FA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return FA_ERR_ALIGN;
   return FA_OK;
