@@ -70,6 +70,11 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;  // per tensor, keeps 64-bit off
 // from its first row with 32-bit byte offsets (row x heads x d x 2 bytes), so
 // one row of all heads must stay below 2^31 / 64 bytes.
 constexpr int64_t kMaxRowElems = int64_t(1) << 22;
+// A dispatch counts at most 2^32 - 1 work-items per grid dimension (its size
+// field is 32-bit). Every grid here spreads its workgroups along x, with at
+// most 256 threads each; checking all of a call's grids before the first launch
+// keeps a failed call from leaving part of its kernels enqueued.
+constexpr int64_t kMaxGroupsX = 0xffffffffLL / 256;
 
 bool head_dim_ok(int d) {
   return d == 32 || d == 64 || d == 96 || d == 128 || d == 192 || d == 256;
@@ -110,6 +115,10 @@ fa_status launch_decode_common(fa::DecodeArgs& a, const void* q, void* o, float*
   const int64_t row_blocks = (int64_t(group) * Nq + 31) / 32;
   // split grid: x = batch, y = parts, z = KV heads x row blocks (y and z at most 65535)
   if (int64_t(kSubPerChunk) * num_splits > 65535 || row_blocks * Hkv > 65535) return FA_ERR_SHAPE;
+  // combine grid: B x ceil(Hq * Nq / rows per workgroup), d / 4 threads per row
+  const int64_t combine_rows = 1024 / d;
+  if (int64_t(B) > kMaxGroupsX || int64_t(B) * ((int64_t(Hq) * Nq + combine_rows - 1) / combine_rows) > kMaxGroupsX)
+    return FA_ERR_SHAPE;
   a.q = q; a.o = o; a.lse = lse;
   const size_t rows = size_t(kSubPerChunk) * num_splits * B * Hq * Nq;
   a.part_o = static_cast<float*>(workspace);
@@ -136,7 +145,7 @@ fa_status fwd_common(fa::FwdArgs& a, int d, int wl, int wr, int causal, float sc
   a.wl = wl;
   a.wr = causal ? 0 : wr;
   const int64_t blocks = int64_t(a.n_qtiles) * a.Hq * a.B;
-  if (blocks > 0x7fffffff) return FA_ERR_SHAPE;
+  if (blocks > kMaxGroupsX) return FA_ERR_SHAPE;
   // K and V bytes each query head reads (a group shares them)
   const int64_t kv_rows = a.cu_k ? int64_t(a.total_k) / a.B : a.Nk;
   a.hb = fa::order_block_heads(int64_t(a.Hq) * a.B, kv_rows * d * 4 / a.group);
@@ -159,9 +168,10 @@ fa_status bwd_common(const void* q, const void* k, const void* v, const void* o,
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
     return FA_ERR_ALIGN;
   const int64_t nkt = (int64_t(Nk) + 127) / 128, nqt = (int64_t(Nq) + 127) / 128;
-  if (nkt * Hkv * B > 0x7fffffffLL || nqt * Hq * B > 0x7fffffffLL) return FA_ERR_SHAPE;
-  // both statistics arrays addressed with 32-bit byte offsets
-  if (bwd_stat_rows(B, Nq, Hq) > 0x0fffffffu) return FA_ERR_SHAPE;
+  if (nkt * Hkv * B > kMaxGroupsX || nqt * Hq * B > kMaxGroupsX) return FA_ERR_SHAPE;
+  // the statistics kernel gives a row up to 32 threads (at least 8 rows per
+  // workgroup); this also keeps the arrays' 32-bit byte offsets in range
+  if ((bwd_stat_rows(B, Nq, Hq) + 7) / 8 > size_t(kMaxGroupsX)) return FA_ERR_SHAPE;
   fa::BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
   a.dq = dq; a.dk = dk; a.dv = dv;

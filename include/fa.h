@@ -75,8 +75,9 @@ typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
  *   lse        : device float32 [B][Hq][Nq] or NULL.
  *   B, Nq, Nk, Hq, Hkv, d : sizes; Nq != Nk is allowed (with causal = 1 the
  *                mask is bottom-right aligned). FA_ERR_SHAPE when a tensor
- *                holds more than 2^40 elements or Hq * d exceeds 2^22 (the
- *                same limits hold for every entry point below).
+ *                holds more than 2^40 elements, Hq * d exceeds 2^22, or one
+ *                of the call's kernel grids would exceed 2^32 - 1 threads
+ *                (the same limits hold for every entry point below).
  *   causal     : 0 or 1 (any non-zero value means 1).
  *   scale      : multiplies Q K^T before the softmax, used exactly as passed
  *                (the pages' default is 1/sqrt(d); the Python layer applies it).

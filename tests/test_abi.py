@@ -54,6 +54,7 @@ def fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Nq=8, Nk=8, Hq=2, Hk
     (dict(B=0), 2), (dict(Nq=0), 2), (dict(Nk=-1), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2),
     (dict(B=1 << 20, Nq=1 << 20, Hq=64, d=256), 2),
     (dict(Hq=1 << 15, Hkv=1 << 15, d=256), 2), (dict(Hq=1 << 17, Hkv=1, d=64), 2),
+    (dict(B=1 << 10, Nq=1 << 17, Hq=16, Hkv=16, d=32), 2),   # 2^24 workgroups of 256 threads
     (dict(Hq=3, Hkv=2), 3),
     (dict(d=48), 4), (dict(d=16), 4), (dict(d=512), 4), (dict(d=0), 4),
     (dict(dtype=2), 5), (dict(dtype=-1), 5),
@@ -93,6 +94,7 @@ def dec(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, Nq=1, Nk=64, Hq=4, H
     (dict(S=0), 6), (dict(S=_lib.FA_MAX_SPLITS + 1), 6),
     (dict(wsb=16), 7), (dict(ws=MIS), 9), (dict(k=MIS), 9), (dict(scale=float("-inf")), 10),
     (dict(Nk=1 << 20, Hkv=8, Hq=8, d=256), 2), (dict(Nk=1, Hq=1 << 15, Hkv=1 << 15, d=256), 2),
+    (dict(B=1 << 20, Hq=512, Hkv=512, d=32, S=1), 2),   # combine grid of 2^24 workgroups
 ])
 def test_decode_rejects_invalid_arguments(lib, kw, status):
     assert dec(lib, **kw) == status
@@ -174,6 +176,7 @@ def bwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE
     (dict(q=None), 1), (dict(o=None), 1), (dict(lse=None), 1), (dict(do=None), 1), (dict(dq=None), 1),
     (dict(dk=None), 1), (dict(dv=None), 1), (dict(ws=None), 1),
     (dict(B=0), 2), (dict(Nk=0), 2), (dict(Hq=1 << 15, Hkv=1 << 15, d=256), 2),
+    (dict(B=1 << 12, Nq=1 << 11, Hq=16, Hkv=16), 2),   # statistics kernel grid of 2^24 workgroups
     (dict(Hq=3, Hkv=2), 3), (dict(d=80), 4), (dict(dtype=4), 5),
     (dict(wsb=16), 7), (dict(do=MIS), 9), (dict(dq=MIS), 9), (dict(dk=MIS), 9), (dict(dv=MIS), 9),
     (dict(ws=MIS), 9), (dict(lse=FAKE + 2), 9), (dict(scale=float("nan")), 10),
