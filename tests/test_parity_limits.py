@@ -81,3 +81,80 @@ def test_decode_at_the_widest_rows(bits, dev):
     o_ref, lse_ref = oracle.attention_bits(qb2[:, :, hs], kb2[:, :, hs], vb2[:, :, hs], DTYPE, scale=scale)
     cmp.check_o(to_np(o[:, :, hs]), o_ref, DTYPE, what)
     cmp.check_lse(to_np(lse[:, hs]), lse_ref, what)
+
+
+# Tensors larger than 4 GiB: every byte offset past the first 4 GiB would wrap in
+# 32 bits. The batches in between only have to hold N(0,1) values, so they are
+# drawn on the device (torch's seeded generator); the first and the last batch
+# hold the shared host recipe's bits and are checked whole against the oracle.
+BIG_WID = 991
+
+
+def big_tensor(tensor_id, shape, dtype, edge_bits):
+    import torch
+    from gpu_util import device
+    dev = device()
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(BIG_WID * 16 + tensor_id)
+    x = torch.empty(shape, dtype=tdt, device=dev)
+    for b0 in range(0, shape[0], 64):
+        n = min(64, shape[0] - b0)
+        x[b0:b0 + n] = torch.randn((n,) + tuple(shape[1:]), generator=g, device=dev, dtype=torch.float32).to(tdt)
+    x[0:1] = to_dev(edge_bits[0:1], dtype)
+    x[-1:] = to_dev(edge_bits[1:2], dtype)
+    torch.cuda.synchronize()
+    return x
+
+
+def big_inputs(shapes, dtype, ids):
+    edges = [synthetic.normal_bits(BIG_WID, t, s, dtype, batches=[0, s[0] - 1]) for t, s in zip(ids, shapes)]
+    return edges, [big_tensor(t, s, dtype, e) for t, s, e in zip(ids, shapes, edges)]
+
+
+def test_forward_and_backward_beyond_4_gib():
+    """B = 600, 1024 tokens, 32 heads of 128, bf16: 4.7 GiB per tensor."""
+    import torch
+    B, N, H, d, dtype = 600, 1024, 32, 128, "bf16"
+    shape = (B, N, H, d)
+    print(f"[limits] forward + backward {shape} {dtype}", flush=True)
+    edges, (q, k, v, do) = big_inputs([shape] * 4, dtype,
+                                      [synthetic.Q_ID, synthetic.K_ID, synthetic.V_ID, synthetic.DO_ID])
+    scale = 1.0 / math.sqrt(d)
+    for causal in (False, True):
+        o, lse = attention(q, k, v, causal=causal, scale=scale)
+        grads = attention_backward(q, k, v, o, lse, do, causal=causal, scale=scale) if causal else None
+        for n, b in enumerate((0, B - 1)):
+            what = f"{shape} {dtype} causal={causal} b={b}"
+            qb, kb, vb, dob = (oracle.widen(e[n:n + 1], dtype) for e in edges)
+            o_ref, lse_ref = oracle.attention(qb, kb, vb, causal=causal, scale=scale)
+            cmp.check_o(to_np(o[b:b + 1]), o_ref, dtype, what)
+            cmp.check_lse(to_np(lse[b:b + 1]), lse_ref, what)
+            if grads is not None:
+                ref = oracle.backward(qb, kb, vb, dob, causal=True, scale=scale)
+                mag = oracle.backward_magnitudes(qb, kb, vb, dob, causal=True, scale=scale)
+                for g, r, m, name in zip(grads, ref, mag, ("dq", "dk", "dv")):
+                    cmp.check_grad(to_np(g[b:b + 1]), r, m, dtype, f"{what} {name}")
+        del o, lse, grads
+    del q, k, v, do
+    torch.cuda.empty_cache()
+
+
+def test_decode_beyond_4_gib():
+    """A cache of 64 sequences of 8300 keys, 32 KV heads of 128, bf16 (4.3 GB per
+    tensor); 128 query heads (groups of 4), one query row each."""
+    import torch
+    B, Nk, Hq, Hkv, d, dtype = 64, 8300, 128, 32, 128, "bf16"
+    print(f"[limits] decode B={B} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} {dtype}", flush=True)
+    edges, (q, k, v) = big_inputs([(B, 1, Hq, d), (B, Nk, Hkv, d), (B, Nk, Hkv, d)], dtype,
+                                  [synthetic.Q_ID, synthetic.K_ID, synthetic.V_ID])
+    scale = 1.0 / math.sqrt(d)
+    o, lse = decode(q, k, v, num_splits=16, scale=scale)
+    for n, b in enumerate((0, B - 1)):
+        what = f"decode B={B} Nk={Nk} Hq={Hq} Hkv={Hkv} b={b}"
+        o_ref, lse_ref = oracle.attention_bits(edges[0][n:n + 1], edges[1][n:n + 1], edges[2][n:n + 1], dtype,
+                                               scale=scale)
+        cmp.check_o(to_np(o[b:b + 1]), o_ref, dtype, what)
+        cmp.check_lse(to_np(lse[b:b + 1]), lse_ref, what)
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
