@@ -63,6 +63,21 @@ def _check(q, k, v):
         raise ValueError("q, k, v must be on one device")
 
 
+def _check_given(name, t, shape, dtype, device):
+    """A caller-supplied output must be exactly what the kernels write into: a smaller,
+    strided or host tensor would let them write outside it."""
+    if t is None:
+        return
+    if (not t.is_cuda or t.device != device or tuple(t.shape) != tuple(shape) or t.dtype != dtype
+            or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}")
+
+
+def _check_on(name, t, device):
+    if not t.is_cuda or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on {device}")
+
+
 def _stream(t):
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
@@ -79,6 +94,8 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
     Nk, Hkv = k.shape[1], k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _check_given("out", out, q.shape, q.dtype, q.device)
+    _check_given("lse", lse, (B, Hq, Nq), torch.float32, q.device)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
     with torch.cuda.device(q.device):
@@ -112,6 +129,9 @@ def decode(q, k_cache, v_cache, num_splits: int = 16, scale: float | None = None
     need = decode_workspace_bytes(B, Nq, Hq, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_on("workspace", workspace, q.device)
+    _check_given("out", out, q.shape, q.dtype, q.device)
+    _check_given("lse", lse, (B, Hq, Nq), torch.float32, q.device)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
     with torch.cuda.device(q.device):
@@ -143,6 +163,9 @@ def decode_paged(q, k_pages, v_pages, block_table, cache_seqlens, num_splits: in
     for name, t in (("block_table", block_table), ("cache_seqlens", cache_seqlens)):
         if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    for name, t in (("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table),
+                    ("cache_seqlens", cache_seqlens)):
+        _check_on(name, t, q.device)
     B, Nq, Hq, d = q.shape
     num_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
     if block_table.dim() != 2 or block_table.shape[0] != B or tuple(cache_seqlens.shape) != (B,):
@@ -152,6 +175,9 @@ def decode_paged(q, k_pages, v_pages, block_table, cache_seqlens, num_splits: in
     need = decode_workspace_bytes(B, Nq, Hq, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_on("workspace", workspace, q.device)
+    _check_given("out", out, q.shape, q.dtype, q.device)
+    _check_given("lse", lse, (B, Hq, Nq), torch.float32, q.device)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
     with torch.cuda.device(q.device):
@@ -187,8 +213,12 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, cau
     total_q, Hq, d = q.shape
     total_k, Hkv = k.shape[0], k.shape[1]
     B = cu_seqlens_q.shape[0] - 1
+    for name, t in (("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        _check_on(name, t, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _check_given("out", out, q.shape, q.dtype, q.device)
+    _check_given("lse", lse, (Hq, total_q), torch.float32, q.device)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
     with torch.cuda.device(q.device):
@@ -212,18 +242,19 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
     torch = _torch()
     _check(q, k, v)
     for name, t in (("o", o), ("dout", dout)):
-        if not t.is_cuda or t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor shaped and typed like q")
+        _check_given(name, t, q.shape, q.dtype, q.device)
     B, Nq, Hq, d = q.shape
     Nk, Hkv = k.shape[1], k.shape[2]
-    if (not lse.is_cuda or lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq)
-            or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 device tensor [B, Hq, Nq]")
+    _check_given("lse", lse, (B, Hq, Nq), torch.float32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = bwd_workspace_bytes(B, Nq, Hq)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_on("workspace", workspace, q.device)
+    _check_given("dq", dq, q.shape, q.dtype, q.device)
+    _check_given("dk", dk, k.shape, k.dtype, q.device)
+    _check_given("dv", dv, v.shape, v.dtype, q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -267,14 +298,19 @@ def attention_varlen_backward(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k,
     total_q, Hq, d = q.shape
     total_k, Hkv = k.shape[0], k.shape[1]
     B = cu_seqlens_q.shape[0] - 1
-    if (not lse.is_cuda or lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, total_q)
-            or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 device tensor [Hq, total_q]")
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("cu_seqlens_q", cu_seqlens_q),
+                    ("cu_seqlens_k", cu_seqlens_k)):
+        _check_on(name, t, q.device)
+    _check_given("lse", lse, (Hq, total_q), torch.float32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = bwd_workspace_bytes(B, int(max_seqlen_q), Hq)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_on("workspace", workspace, q.device)
+    _check_given("dq", dq, q.shape, q.dtype, q.device)
+    _check_given("dk", dk, k.shape, k.dtype, q.device)
+    _check_given("dv", dv, v.shape, v.dtype, q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
