@@ -229,8 +229,9 @@ def main():
                     help="also run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the units "
+              "(batch, KV head) are independent, so a sharded run is N copies of this one). "
+              "Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import numpy as np
