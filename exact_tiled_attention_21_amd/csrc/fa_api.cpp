@@ -129,7 +129,10 @@ fa_status launch_decode_common(fa::DecodeArgs& a, const void* q, void* o, float*
   a.sub_per = units >= kDecodeWaves ? 1 : (2 * units >= kDecodeWaves ? 2 : kSubPerChunk);
   a.splits = a.sub_per * num_splits;
   a.row_blocks = static_cast<int>(row_blocks);
-  a.sl2 = scale * 1.4426950408889634f;
+  // the kernels take the reference max of the raw scores times sl2, which must not
+  // be negative: a negative scale is applied by flipping the sign of q (exact)
+  a.sl2 = fabsf(scale) * 1.4426950408889634f;
+  a.negate_q = scale < 0.f;
   hipError_t e = fa::launch_decode(a, d, dtype == FA_BF16, causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

@@ -98,6 +98,12 @@ template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
                   ((static_cast<size_t>(b) * a.Nq + ri) * a.Hq + rhq) * D + 8 * hh;
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) qf[s] = rvalid ? *reinterpret_cast<const V8*>(qp + 16 * s) : V8{};
+    // a negative scale: scores of -q against |scale|, so the row max taken below is
+    // the max of the scaled scores
+    if (a.negate_q) {
+#pragma unroll
+      for (int s = 0; s < C::NS; ++s) qf[s] = -qf[s];
+    }
 
     // tiles of this part: the keys are cut into 32-key tiles and part p of the
     // nparts parts takes tiles p, p + nparts, p + 2 nparts, ... below k_hi (the

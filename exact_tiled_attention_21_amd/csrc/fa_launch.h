@@ -42,7 +42,8 @@ struct DecodeArgs {
   int splits;      // parts (partials per row): sub_per parts per requested split
   int sub_per;     // parts per requested split: 1, 2 or 4
   int row_blocks;  // ceil(group * Nq / 32)
-  float sl2;       // scale * log2(e)
+  float sl2;       // |scale| * log2(e)
+  int negate_q;    // scale < 0: the kernel flips the sign of q instead
   // paged cache (block_table non-null): k and v point at page pools
   // [num_pages][page_size][Hkv][d]; sequence b owns pages block_table[b][0..max_pages)
   // and seqlens[b] keys. For a contiguous cache block_table and seqlens are null.

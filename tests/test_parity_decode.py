@@ -24,16 +24,16 @@ def inputs(wid, B, Nq, Nk, Hq, Hkv, d, dtype):
     return qb, kb, vb
 
 
-def run(wid, B, Nq, Nk, Hq, Hkv, d, dtype, splits, causal=False, ref=None):
+def run(wid, B, Nq, Nk, Hq, Hkv, d, dtype, splits, causal=False, ref=None, scale=None):
     qb, kb, vb = inputs(wid, B, Nq, Nk, Hq, Hkv, d, dtype)
-    scale = 1.0 / math.sqrt(d)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
     print(f"[decode] wid={wid} B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} {dtype} S={splits} "
-          f"causal={causal}", flush=True)
+          f"causal={causal} scale={scale}", flush=True)
     o, lse = decode(to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype), num_splits=splits,
                     causal=causal, scale=scale)
     if ref is None:
         ref = oracle.attention_bits(qb, kb, vb, dtype, causal=causal, scale=scale)
-    what = f"decode B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} S={splits} causal={causal}"
+    what = f"decode B={B} Nq={Nq} Nk={Nk} Hq={Hq} Hkv={Hkv} d={d} S={splits} causal={causal} scale={scale}"
     st = cmp.check_o(to_np(o), ref[0], dtype, what)
     cmp.check_lse(to_np(lse), ref[1], what)
     return st, ref, o
@@ -83,6 +83,19 @@ def test_odd_batch_and_row_blocks(case):
     and per-batch row counts that leave the combine's last workgroup partly idle."""
     B, Nq, Hq, Hkv, d, dtype, causal = case
     run(950 + B + Nq, B, Nq, 900, Hq, Hkv, d, dtype, 8, causal=causal)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("scale", [-1.0, "-1/sqrt(d)"])
+def test_negative_scale(dtype, causal, scale):
+    """A negative scale is used as passed: the softmax of -|scale| q.k. With
+    scale = -1 at d = 64 the raw scores spread over tens of units, so a reference
+    max taken from the unscaled scores would put probabilities far above the fp16
+    range; the oracle decides."""
+    d = 64
+    sc = -1.0 / math.sqrt(d) if scale != -1.0 else -1.0
+    run(1100 + (dtype == "bf16") + 2 * causal, 2, 3, 1500, 8, 2, d, dtype, 16, causal=causal, scale=sc)
 
 
 def test_decode_matches_forward():

@@ -35,19 +35,19 @@ def gathered(pool_bits, bt, page_size):
     return pool_bits[bt.reshape(-1)].reshape(B, P * page_size, *pool_bits.shape[2:])
 
 
-def run(wid, B, Nq, Hq, Hkv, d, dtype, page_size, max_pages, lens, splits=16, causal=False):
+def run(wid, B, Nq, Hq, Hkv, d, dtype, page_size, max_pages, lens, splits=16, causal=False, scale=None):
     import torch
     qb, kp, vp, bt, lens = paged_case(wid, B, Nq, Hq, Hkv, d, dtype, page_size, max_pages, lens)
-    scale = 1.0 / math.sqrt(d)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
     print(f"[paged] wid={wid} B={B} Nq={Nq} Hq={Hq} Hkv={Hkv} d={d} {dtype} page={page_size} "
-          f"max_pages={max_pages} lens={lens.tolist()} S={splits} causal={causal}", flush=True)
+          f"max_pages={max_pages} lens={lens.tolist()} S={splits} causal={causal} scale={scale}", flush=True)
     dev = device()
     o, lse = decode_paged(to_dev(qb, dtype), to_dev(kp, dtype), to_dev(vp, dtype),
                           torch.from_numpy(bt).to(dev), torch.from_numpy(lens).to(dev),
                           num_splits=splits, causal=causal, scale=scale)
     ref = oracle.attention_bits(qb, gathered(kp, bt, page_size), gathered(vp, bt, page_size), dtype,
                                 causal=causal, scale=scale, seqlens_k=lens)
-    what = f"paged page={page_size} lens={lens.tolist()} S={splits} causal={causal} d={d}"
+    what = f"paged page={page_size} lens={lens.tolist()} S={splits} causal={causal} d={d} scale={scale}"
     st = cmp.check_o(to_np(o), ref[0], dtype, what)
     cmp.check_lse(to_np(lse), ref[1], what)
     return st, to_np(o), to_np(lse)
@@ -125,3 +125,12 @@ def test_out_of_range_page_reads_zeros_without_leaving_the_pool():
         cmp.check_o(to_np(o)[b:b + 1], ref[0][b:b + 1], "bf16", f"seq {b}")
         cmp.check_lse(to_np(lse)[b:b + 1], ref[1][b:b + 1], f"seq {b}")
     assert np.all(np.isfinite(to_np(o)[1]))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("scale", [-1.0, -0.125])
+def test_paged_negative_scale(dtype, scale):
+    """A negative scale over a paged cache (d = 64, so -0.125 is -1/sqrt(d)), causal
+    with ragged lengths: the oracle decides."""
+    run(2300 + (dtype == "bf16") + 2 * (scale == -1.0), 3, 2, 8, 2, 64, dtype, 64, 12, [700, 64, 333],
+        splits=8, causal=True, scale=scale)

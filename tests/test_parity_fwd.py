@@ -115,6 +115,17 @@ def test_scale_is_used_as_passed():
     run_full(301, 1, 130, 130, 2, 2, 64, "bf16", True, scale=0.0)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,scale", [(64, -1.0), (128, "-1/sqrt(d)"), (256, "-1/sqrt(d)")])
+def test_negative_scale(dtype, causal, d, scale):
+    """O and LSE at a negative scale (the softmax of -|scale| q.k; the kernel flips
+    the sign of Q and uses |scale|), several tiles and ragged tails, GQA heads."""
+    sc = -1.0 if scale == -1.0 else -1.0 / math.sqrt(d)
+    run_full(320 + 4 * (d // 64) + 2 * (dtype == "bf16") + int(causal), 2, 300, 333, 6, 2, d, dtype, causal,
+             scale=sc)
+
+
 def run_sampled(w, seed):
     """Whole workload on the GPU; oracle on sampled rows of b = 0 and b = B-1."""
     q, k, v = w.inputs()
@@ -145,15 +156,21 @@ def run_sampled(w, seed):
     print(f"[fwd sampled] {w.name}: {cmp.fmt(worst)}", flush=True)
 
 
-def test_headline_full_batch0_and_sampled():
+def test_headline_whole_workload():
+    """The pages' headline workload [16, 1024, 32, 128] f16 run once on the GPU in the
+    benchmark's launch configuration and compared with the oracle on every element of
+    every batch; then the secondary rule on sampled rows of the first and last batch."""
     w = synthetic.WORKLOADS["headline_f16_1024"]
     q, k, v = w.inputs()
-    print(f"[fwd] {w.name}", flush=True)
+    print(f"[fwd] {w.name} whole", flush=True)
     o, lse = attention(to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, w.dtype), causal=False, scale=w.scale)
-    o_np, lse_np = to_np(o[:1]), to_np(lse[:1])
-    o_ref, lse_ref = oracle.attention_bits(q[:1], k[:1], v[:1], w.dtype, scale=w.scale)
-    cmp.check_o(o_np, o_ref, w.dtype, "headline b=0 whole")
-    cmp.check_lse(lse_np, lse_ref, "headline b=0 whole")
+    o_np, lse_np = to_np(o), to_np(lse)
+    del o, lse
+    o_ref, lse_ref = oracle.attention_bits(q, k, v, w.dtype, scale=w.scale)
+    st = cmp.check_o(o_np, o_ref, w.dtype, "headline whole")
+    cmp.check_lse(lse_np, lse_ref, "headline whole")
+    print(f"[fwd] {w.name} whole: {cmp.fmt(st)}", flush=True)
+    del o_np, o_ref
     run_sampled(w, 7)
 
 
