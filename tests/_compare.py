@@ -18,10 +18,12 @@ error of at most about u M; a float32 emulation of that arithmetic reaches
 0.84 u M on the test shapes, and a dropped D term, a causal mask one key off
 or two swapped dO rows exceed the bound 3x to 10^5x.
 
-Secondary rule (the upstream test criterion: error at most twice that of a
-plain implementation): max error <= 2 * max error of a float32 emulation
-(fp32 scores and softmax, P rounded to the input type, fp32 P V, O rounded)
-plus one output ulp of slack for the rounding of O itself.
+Secondary rule (the upstream test criterion, "flash-attention-v100" README,
+Tests: the output and the gradients have at most twice the error of a baseline
+implementation): max error <= 2 * max error of a float32 emulation (fp32 scores
+and softmax, P rounded to the input type, fp32 P V, O rounded; for the
+gradients the same arithmetic as emulate_backward) plus one output ulp of slack
+for the rounding of the result itself.
 """
 from __future__ import annotations
 
@@ -63,15 +65,23 @@ UNIT_ROUNDOFF = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
 GRAD_BOUND = 2.0
 
 
+def grad_ratios(g_gpu, g_ref, mag, dtype):
+    """Per element: (|G - G_ref| - ulp(G_ref)/2) / (u M), 0 where within half an ulp."""
+    g_gpu = np.asarray(g_gpu, np.float64)
+    g_ref = np.asarray(g_ref, np.float64)
+    excess = np.abs(g_gpu - g_ref) - 0.5 * ulp(g_ref, dtype)
+    bound = UNIT_ROUNDOFF[dtype] * np.asarray(mag, np.float64)
+    return np.where(excess > 0, excess / np.maximum(bound, 1e-300), 0.0)
+
+
 def check_grad(g_gpu, g_ref, mag, dtype, what=""):
     """Element-wise rounding-error bound on a gradient (rule above)."""
     g_gpu = np.asarray(g_gpu, np.float64)
     g_ref = np.asarray(g_ref, np.float64)
     assert g_gpu.shape == g_ref.shape, (g_gpu.shape, g_ref.shape)
     assert np.all(np.isfinite(g_gpu)), f"{what}: non-finite gradient"
-    excess = np.abs(g_gpu - g_ref) - 0.5 * ulp(g_ref, dtype)
     bound = UNIT_ROUNDOFF[dtype] * np.asarray(mag, np.float64)
-    ratio = np.where(excess > 0, excess / np.maximum(bound, 1e-300), 0.0)
+    ratio = grad_ratios(g_gpu, g_ref, mag, dtype)
     worst = float(ratio.max()) if ratio.size else 0.0
     if worst > GRAD_BOUND:
         i = np.unravel_index(int(ratio.argmax()), ratio.shape)
@@ -119,6 +129,67 @@ def emulate_rows(q, k, v, rows, h, causal, scale, dtype, nq):
     l = p.sum(axis=1, keepdims=True)
     o = (_round_to(p, dtype) @ v32) / np.where(l > 0, l, 1)
     return _round_to(o, dtype).astype(np.float64)
+
+
+def _visible(nq, nk, causal, window):
+    i = np.arange(nq)[:, None]
+    j = np.arange(nk)[None, :]
+    diag = i + nk - nq
+    m = np.ones((nq, nk), bool)
+    if causal:
+        m &= j <= diag
+    if window[0] >= 0:
+        m &= j >= diag - window[0]
+    if window[1] >= 0:
+        m &= j <= diag + window[1]
+    return m
+
+
+def emulate_backward(q, k, v, do, causal, scale, dtype, window=(-1, -1)):
+    """Float32 baseline of the gradients: q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d], do like q
+    (exact 16-bit values as float64). A plain low-precision implementation of the
+    same arithmetic: fp32 scores and softmax, O rounded to the input type and
+    D = rowsum(dO * O) from it, P and dS rounded to the input type as product
+    operands, fp32 products and sums, gradients rounded to the input type; a KV
+    head sums its query heads' terms in fp32 before rounding."""
+    q32, k32, v32, do32 = (np.asarray(x, np.float32) for x in (q, k, v, do))
+    B, Nq, Hq, d = q32.shape
+    Nk, Hkv = k32.shape[1], k32.shape[2]
+    group = Hq // Hkv
+    vis = _visible(Nq, Nk, causal, window)
+    has = vis.any(axis=1)
+    sc = np.float32(scale)
+    dq = np.zeros((B, Nq, Hq, d), np.float32)
+    dk = np.zeros((B, Nk, Hkv, d), np.float32)
+    dv = np.zeros((B, Nk, Hkv, d), np.float32)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            qh, kh, vh, doh = q32[b, :, h], k32[b, :, g], v32[b, :, g], do32[b, :, h]
+            s = np.where(vis, (qh @ kh.T) * sc, -np.inf).astype(np.float32)
+            m = np.where(has, s.max(axis=1), 0).astype(np.float32)
+            e = np.where(vis, np.exp(s - m[:, None]), 0).astype(np.float32)
+            p = (e / np.where(has, e.sum(axis=1), 1)[:, None]).astype(np.float32)
+            o = _round_to(_round_to(p, dtype) @ vh, dtype)
+            dp = doh @ vh.T
+            dd = (doh * o).sum(axis=1, dtype=np.float32)
+            ds = (p * (dp - dd[:, None])).astype(np.float32)
+            dq[b, :, h] = sc * (_round_to(ds, dtype) @ kh)
+            dk[b, :, g] += sc * (_round_to(ds, dtype).T @ qh)
+            dv[b, :, g] += _round_to(p, dtype).T @ doh
+    return tuple(_round_to(x, dtype).astype(np.float64) for x in (dq, dk, dv))
+
+
+def check_grad_vs_baseline(g_gpu, g_ref, g_base, dtype, what=""):
+    """The pages' test criterion on a gradient tensor: its maximum error against the
+    fp64 oracle is at most twice that of the plain float32 baseline, plus one output
+    ulp of the largest reference value for the rounding of the gradient itself."""
+    g_gpu, g_ref, g_base = (np.asarray(x, np.float64) for x in (g_gpu, g_ref, g_base))
+    e_gpu = float(np.abs(g_gpu - g_ref).max()) if g_ref.size else 0.0
+    e_base = float(np.abs(g_base - g_ref).max()) if g_ref.size else 0.0
+    slack = float(ulp(np.abs(g_ref).max(), dtype)) if g_ref.size else 0.0
+    assert e_gpu <= 2 * e_base + slack, f"{what}: max error {e_gpu:.3g} > 2 x baseline {e_base:.3g} + {slack:.3g}"
+    return e_gpu, e_base
 
 
 def sample_rows(n: int, rng: np.random.Generator, extra: int = 64):
