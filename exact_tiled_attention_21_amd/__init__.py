@@ -191,12 +191,23 @@ def decode_paged(q, k_pages, v_pages, block_table, cache_seqlens, num_splits: in
     return o, lse_t
 
 
+def _check_max_seqlen(cu, max_seqlen, name):
+    """Every sequence of the prefix sums `cu` is at most max_seqlen long (one
+    device-to-host read of the prefix sums)."""
+    longest = int((cu[1:] - cu[:-1]).max().item()) if cu.numel() > 1 else 0
+    if longest > int(max_seqlen):
+        raise ValueError(f"{name} = {max_seqlen} is below the longest sequence ({longest} rows)")
+
+
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
-                     scale: float | None = None, out=None, lse=None):
+                     scale: float | None = None, out=None, lse=None, validate: bool = True):
     """Exact attention over a packed batch of variable-length sequences.
 
     q [total_q, Hq, d], k/v [total_k, Hkv, d]; cu_seqlens_q/k int32 [B + 1] prefix
-    sums on the device; returns o like q and lse float32 [Hq, total_q]."""
+    sums on the device; returns o like q and lse float32 [Hq, total_q].
+    max_seqlen_q must be at least every sequence's query count; validate=True
+    checks that (one read of the prefix sums to the host), validate=False trusts
+    the caller."""
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda or t.dim() != 3 or not t.is_contiguous():
@@ -217,6 +228,8 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, cau
         _check_on(name, t, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if validate:
+        _check_max_seqlen(cu_seqlens_q, max_seqlen_q, "max_seqlen_q")
     _check_given("out", out, q.shape, q.dtype, q.device)
     _check_given("lse", lse, (Hq, total_q), torch.float32, q.device)
     o = torch.empty_like(q) if out is None else out
@@ -277,11 +290,12 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
 
 def attention_varlen_backward(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
                               max_seqlen_k: int, causal: bool = False, scale: float | None = None,
-                              workspace=None, dq=None, dk=None, dv=None):
+                              workspace=None, dq=None, dk=None, dv=None, validate: bool = True):
     """Gradients of attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, ...) for dout.
 
     q, o, dout [total_q, Hq, d]; k, v [total_k, Hkv, d]; lse float32 [Hq, total_q] as
-    attention_varlen returns it; max_seqlen_q/k at least every sequence's length."""
+    attention_varlen returns it; max_seqlen_q/k at least every sequence's length
+    (validate=True checks that with one read of the prefix sums to the host)."""
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         if not t.is_cuda or t.dim() != 3 or not t.is_contiguous():
@@ -304,6 +318,9 @@ def attention_varlen_backward(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k,
     _check_given("lse", lse, (Hq, total_q), torch.float32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if validate:
+        _check_max_seqlen(cu_seqlens_q, max_seqlen_q, "max_seqlen_q")
+        _check_max_seqlen(cu_seqlens_k, max_seqlen_k, "max_seqlen_k")
     need = bwd_workspace_bytes(B, int(max_seqlen_q), Hq)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

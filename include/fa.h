@@ -117,8 +117,11 @@ fa_status fa_fwd_window(const void* q, const void* k, const void* v, void* o, fl
  *                   at 0 and ending at total_q / total_k. Values are clamped to
  *                   [0, total]; a malformed table gives undefined results for
  *                   the affected sequences but no access outside the tensors.
- *   max_seqlen_q  : the longest query count (sizes the grid; rows beyond a
- *                   sequence's own count are not computed).
+ *   max_seqlen_q  : at least the longest query count (it sizes the grid; rows
+ *                   beyond a sequence's own count are not computed). A value
+ *                   below some sequence's query count leaves that sequence's
+ *                   rows from ceil(max_seqlen_q / 128) * 128 on unwritten (no
+ *                   access outside the tensors); the Python binding checks it.
  *   causal        : bottom-right aligned per sequence, as in fa_fwd. A
  *                   sequence with no key gets O = 0 and LSE = -inf.
  * Status: FA_ERR_NULLPTR for a NULL prefix-sum array, FA_ERR_ALIGN for a
@@ -258,7 +261,12 @@ fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void*
  *   cu_seqlens_k   : device int32 [B + 1], as for fa_fwd_varlen.
  *   max_seqlen_q,
  *   max_seqlen_k   : at least every sequence's query / key count (they size the
- *                    grid and the workspace; longer sequences are clipped).
+ *                    grid and the workspace). A smaller value clips the longer
+ *                    sequences to their first max_seqlen rows / keys, which moves
+ *                    their causal diagonal: their gradients are then those of the
+ *                    clipped problem, not of fa_fwd_varlen's result (no access
+ *                    outside the tensors or the workspace); the Python binding
+ *                    checks the lengths.
  *   workspace      : fa_bwd_workspace_bytes(B, max_seqlen_q, Hq) bytes.
  * Rows of dq, dk, dv outside every sequence are not written. Status:
  * FA_ERR_NULLPTR for a NULL prefix-sum array, FA_ERR_ALIGN for a misaligned one,

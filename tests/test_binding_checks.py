@@ -76,3 +76,22 @@ def test_varlen_index_tensors_on_the_device(qkv):
         attention_varlen(qp, kp, vp, cu, cu.cuda(), 70)
     o, _ = attention_varlen(qp, kp, vp, cu.cuda(), cu.cuda(), 70)
     assert torch.equal(o.reshape(q.shape), attention(q, k, v)[0])
+
+
+def test_varlen_max_seqlen_below_a_sequence_is_refused(qkv):
+    """max_seqlen_q / max_seqlen_k sizes the grid and the workspace; one below some
+    sequence's length would leave rows unwritten (forward) or clip that sequence
+    (backward), so the binding checks it against the prefix sums."""
+    from exact_tiled_attention_21_amd import attention_varlen_backward
+    q, k, v = qkv
+    qp, kp, vp = (x.reshape(140, 4, 64) for x in (q, k, v))
+    cu = torch.tensor([0, 30, 140], dtype=torch.int32, device="cuda")   # lengths 30 and 110
+    with pytest.raises(ValueError, match="max_seqlen_q"):
+        attention_varlen(qp, kp, vp, cu, cu, 100)
+    o, lse = attention_varlen(qp, kp, vp, cu, cu, 110)
+    do = torch.ones_like(qp)
+    with pytest.raises(ValueError, match="max_seqlen_q"):
+        attention_varlen_backward(qp, kp, vp, o, lse, do, cu, cu, 100, 110)
+    with pytest.raises(ValueError, match="max_seqlen_k"):
+        attention_varlen_backward(qp, kp, vp, o, lse, do, cu, cu, 110, 100)
+    attention_varlen_backward(qp, kp, vp, o, lse, do, cu, cu, 110, 110)
