@@ -97,8 +97,10 @@ def test_malformed_prefix_sums_stay_inside_the_tensors():
     bad_q = np.array([0, 100, 150, 1 << 30], np.int32)
     bad_k = np.array([0, 100, -7, 1 << 30], np.int32)
     dev = device()
+    # validate=False: the binding's length check would refuse these tables before the library
     o, lse = attention_varlen(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"),
-                              torch.from_numpy(bad_q).to(dev), torch.from_numpy(bad_k).to(dev), 200)
+                              torch.from_numpy(bad_q).to(dev), torch.from_numpy(bad_k).to(dev), 200,
+                              validate=False)
     torch.cuda.synchronize()
     ro, rl = oracle.attention_bits(qb[None, :100], kb[None, :100], vb[None, :100], "bf16",
                                    scale=1.0 / math.sqrt(64))
