@@ -7,6 +7,8 @@ kernels of libfa.so. torch supplies device memory and the current stream.
   attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                    causal=False, scale=None) -> (o, lse)
   decode(q, k_cache, v_cache, num_splits=16, scale=None, causal=False) -> (o, lse)
+  decode_noalloc(q, k_cache, v_cache, num_splits=16, scale=None, causal=False,
+                 out=None, lse=None) -> (o, lse)
   decode_paged(q, k_pages, v_pages, block_table, cache_seqlens, num_splits=16,
                scale=None, causal=False) -> (o, lse)
   attention_backward(q, k, v, o, lse, dout, causal=False, scale=None,
@@ -24,10 +26,10 @@ from __future__ import annotations
 import ctypes
 import math
 
-from ._lib import FA_BF16, FA_F16, FA_MAX_SPLITS, FaError, load, status_str  # noqa: F401
+from ._lib import FA_BF16, FA_F16, FA_MAX_SPLITS, FA_NOALLOC_SCRATCH_BYTES, FaError, load, status_str  # noqa: F401
 
 __all__ = ["attention", "attention_varlen", "attention_backward", "attention_varlen_backward", "attention_func",
-           "bwd_workspace_bytes", "decode",
+           "bwd_workspace_bytes", "decode", "decode_noalloc",
            "decode_paged", "decode_workspace_bytes", "FaError", "load"]
 
 
@@ -142,6 +144,31 @@ def decode(q, k_cache, v_cache, num_splits: int = 16, scale: float | None = None
                                       _stream(q))
     if st != 0:
         raise FaError(st, "fa_decode_splitkv")
+    return o, lse_t
+
+
+def decode_noalloc(q, k_cache, v_cache, num_splits: int = 16, scale: float | None = None,
+                   causal: bool = False, out=None, lse=None):
+    """decode() through fa_decode_splitkv_noalloc: the library takes the partials from
+    a fixed device array instead of a workspace (calls that overlap on one GPU race
+    on it). With out and lse given, nothing is allocated on this path."""
+    torch = _torch()
+    _check(q, k_cache, v_cache)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check_given("out", out, q.shape, q.dtype, q.device)
+    _check_given("lse", lse, (B, Hq, Nq), torch.float32, q.device)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    with torch.cuda.device(q.device):
+        st = load().fa_decode_splitkv_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                              o.data_ptr(), lse_t.data_ptr(), B, Nq, Nk, Hq, Hkv, d,
+                                              int(num_splits), int(bool(causal)), float(scale),
+                                              _dtype_code(q), _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_decode_splitkv_noalloc")
     return o, lse_t
 
 

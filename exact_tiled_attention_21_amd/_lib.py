@@ -10,9 +10,10 @@ FA_F16, FA_BF16 = 0, 1
 FA_MAX_SPLITS = 256
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULLPTR", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADS", 4: "FA_ERR_HEADDIM",
           5: "FA_ERR_DTYPE", 6: "FA_ERR_SPLITS", 7: "FA_ERR_WORKSPACE", 8: "FA_ERR_LAUNCH",
-          9: "FA_ERR_ALIGN", 10: "FA_ERR_SCALE"}
+          9: "FA_ERR_ALIGN", 10: "FA_ERR_SCALE", 11: "FA_ERR_SCRATCH"}
+FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 EXPORTS = ("fa_fwd", "fa_fwd_window", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_splitkv",
-           "fa_decode_splitkv_paged", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_window", "fa_bwd_varlen",
+           "fa_decode_splitkv_noalloc", "fa_decode_splitkv_paged", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_window", "fa_bwd_varlen",
            "fa_status_str")
 
 _lib = None
@@ -44,6 +45,8 @@ def load(path: str = LIB_PATH):
     lib.fa_decode_workspace_bytes.restype = S
     lib.fa_decode_splitkv.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, S, P]
     lib.fa_decode_splitkv.restype = I
+    lib.fa_decode_splitkv_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P]
+    lib.fa_decode_splitkv_noalloc.restype = I
     lib.fa_decode_splitkv_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, P, S, P]
     lib.fa_decode_splitkv_paged.restype = I
     lib.fa_bwd_workspace_bytes.argtypes = [I, I, I]

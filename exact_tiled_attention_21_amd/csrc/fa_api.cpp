@@ -50,6 +50,8 @@ hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, bool causal, hip
   return hipErrorInvalidValue;
 }
 
+fa_status noalloc_scratch(void** ptr, size_t* bytes);   // fa_noalloc.hip
+
 hipError_t launch_bwd(const BwdArgs& a, int d, bool bf16, bool band, hipStream_t s) {
   switch (d) {
     case 32: return launch_bwd_d32(a, bf16, band, s);
@@ -106,11 +108,27 @@ constexpr int kSubPerChunk = 4;
 // single-wave workgroups that give the chip about one round (256 CUs x 4 SIMDs)
 constexpr int64_t kDecodeWaves = 1024;
 
+// Parts per requested split: 1, 2 or 4, so that the split grid has about
+// kDecodeWaves single-wave workgroups.
+int decode_sub_per(int B, int Nq, int Hq, int Hkv, int num_splits) {
+  const int64_t row_blocks = (int64_t(Hq / Hkv) * Nq + 31) / 32;
+  const int64_t units = int64_t(num_splits) * Hkv * row_blocks * B;
+  return units >= kDecodeWaves ? 1 : (2 * units >= kDecodeWaves ? 2 : kSubPerChunk);
+}
+
+// Bytes of partials for `slices` part slices: float32 [slices][B][Hq][Nq][d]
+// then float32 [slices][B][Hq][Nq], each padded to 256 bytes.
+size_t decode_partial_bytes(int64_t slices, int B, int Nq, int Hq, int d) {
+  const size_t rows = size_t(slices) * B * Hq * Nq;
+  return pad256(rows * d * sizeof(float)) + pad256(rows * sizeof(float));
+}
+
 // Fills the rest of the decode arguments (cache fields already set), checks the
-// grid limits and enqueues the split and combine kernels.
+// grid limits and enqueues the split and combine kernels. The workspace holds
+// `slices` part slices of partials (at least the parts this call uses).
 fa_status launch_decode_common(fa::DecodeArgs& a, const void* q, void* o, float* lse, int B, int Nq,
                                int Hq, int Hkv, int d, int num_splits, int causal, float scale,
-                               fa_dtype dtype, void* workspace, void* stream) {
+                               fa_dtype dtype, void* workspace, int64_t slices, void* stream) {
   const int group = Hq / Hkv;
   const int64_t row_blocks = (int64_t(group) * Nq + 31) / 32;
   // split grid: x = batch, y = parts, z = KV heads x row blocks (y and z at most 65535)
@@ -120,13 +138,12 @@ fa_status launch_decode_common(fa::DecodeArgs& a, const void* q, void* o, float*
   if (int64_t(B) > kMaxGroupsX || int64_t(B) * ((int64_t(Hq) * Nq + combine_rows - 1) / combine_rows) > kMaxGroupsX)
     return FA_ERR_SHAPE;
   a.q = q; a.o = o; a.lse = lse;
-  const size_t rows = size_t(kSubPerChunk) * num_splits * B * Hq * Nq;
+  const size_t rows = size_t(slices) * B * Hq * Nq;
   a.part_o = static_cast<float*>(workspace);
   a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pad256(rows * d * sizeof(float)));
   a.B = B; a.Nq = Nq; a.Hq = Hq; a.Hkv = Hkv;
   a.group = group;
-  const int64_t units = int64_t(num_splits) * Hkv * row_blocks * B;
-  a.sub_per = units >= kDecodeWaves ? 1 : (2 * units >= kDecodeWaves ? 2 : kSubPerChunk);
+  a.sub_per = decode_sub_per(B, Nq, Hq, Hkv, num_splits);
   a.splits = a.sub_per * num_splits;
   a.row_blocks = static_cast<int>(row_blocks);
   // the kernels take the reference max of the raw scores times sl2, which must not
@@ -239,8 +256,7 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
 size_t fa_decode_workspace_bytes(int B, int Nq, int Hq, int d, int num_splits) {
   if (B < 1 || Nq < 1 || Hq < 1 || !head_dim_ok(d) || num_splits < 1 || num_splits > FA_MAX_SPLITS)
     return 0;
-  const size_t rows = size_t(kSubPerChunk) * num_splits * B * Hq * Nq;
-  return pad256(rows * d * sizeof(float)) + pad256(rows * sizeof(float));
+  return decode_partial_bytes(int64_t(kSubPerChunk) * num_splits, B, Nq, Hq, d);
 }
 
 fa_status fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache, void* o,
@@ -261,7 +277,7 @@ fa_status fa_decode_splitkv(const void* q, const void* k_cache, const void* v_ca
   a.block_table = nullptr; a.seqlens = nullptr;
   a.page_size = 0; a.max_pages = 0; a.num_pages = 0;
   return launch_decode_common(a, q, o, lse, B, Nq, Hq, Hkv, d, num_splits, causal, scale, dtype,
-                              workspace, stream);
+                              workspace, int64_t(kSubPerChunk) * num_splits, stream);
 }
 
 fa_status fa_decode_splitkv_paged(const void* q, const void* k_pages, const void* v_pages,
@@ -293,7 +309,33 @@ fa_status fa_decode_splitkv_paged(const void* q, const void* k_pages, const void
   a.block_table = block_table; a.seqlens = cache_seqlens;
   a.page_size = page_size; a.max_pages = max_pages_per_seq; a.num_pages = num_pages;
   return launch_decode_common(a, q, o, lse, B, Nq, Hq, Hkv, d, num_splits, causal, scale, dtype,
-                              workspace, stream);
+                              workspace, int64_t(kSubPerChunk) * num_splits, stream);
+}
+
+fa_status fa_decode_splitkv_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
+                                    float* lse, int B, int Nq, int Nk, int Hq, int Hkv, int d,
+                                    int num_splits, int causal, float scale, fa_dtype dtype, void* stream) {
+  // fa_decode_splitkv's checks, in its order, with the fixed scratch in place of
+  // the workspace; the size check comes before the first HIP call
+  fa_status st = check_common(q, k_cache, v_cache, o, lse, B, Nq, Nk, Hq, Hkv, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
+  if (int64_t(Nk) * Hkv * d * 2 > 0x7fffffffLL) return FA_ERR_SHAPE;   // 32-bit buffer offsets
+  // only the parts this call uses: the scratch layout follows the call
+  const int64_t slices = int64_t(decode_sub_per(B, Nq, Hq, Hkv, num_splits)) * num_splits;
+  if (decode_partial_bytes(slices, B, Nq, Hq, d) > size_t(FA_NOALLOC_SCRATCH_BYTES)) return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  st = fa::noalloc_scratch(&ws, &ws_bytes);
+  if (st != FA_OK) return st;
+  if (decode_partial_bytes(slices, B, Nq, Hq, d) > ws_bytes) return FA_ERR_SCRATCH;
+  fa::DecodeArgs a;
+  a.k = k_cache; a.v = v_cache;
+  a.Nk = Nk;
+  a.block_table = nullptr; a.seqlens = nullptr;
+  a.page_size = 0; a.max_pages = 0; a.num_pages = 0;
+  return launch_decode_common(a, q, o, lse, B, Nq, Hq, Hkv, d, num_splits, causal, scale, dtype, ws, slices,
+                              stream);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int Nq, int Hq) {
@@ -351,6 +393,7 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA_ERR_SCALE: return "scale is not finite";
+    case FA_ERR_SCRATCH: return "the call needs more than the FA_NOALLOC_SCRATCH_BYTES of fixed scratch";
   }
   return "unknown status";
 }

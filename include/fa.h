@@ -61,7 +61,8 @@ typedef enum {
   FA_ERR_WORKSPACE = 7, /* workspace_bytes below the *_workspace_bytes size  */
   FA_ERR_LAUNCH = 8,    /* the HIP runtime rejected a kernel launch         */
   FA_ERR_ALIGN = 9,     /* a tensor pointer is not 16-byte aligned          */
-  FA_ERR_SCALE = 10     /* scale is not a finite number                     */
+  FA_ERR_SCALE = 10,    /* scale is not a finite number                     */
+  FA_ERR_SCRATCH = 11   /* the call needs more than the fixed scratch holds  */
 } fa_status;
 
 typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
@@ -167,6 +168,29 @@ fa_status fa_decode_splitkv(const void* q, const void* k_cache, const void* v_ca
                             float* lse, int B, int Nq, int Nk, int Hq, int Hkv, int d,
                             int num_splits, int causal, float scale, fa_dtype dtype,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_decode_splitkv for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same kernels and the same result, bit for bit, with
+ * the per-part partials in a fixed device array of FA_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each GPU until the process ends. No allocation,
+ * free or allocating library routine is called.
+ *   Arguments, layouts and status codes as fa_decode_splitkv without the
+ *   workspace. FA_ERR_SCRATCH (before any HIP call) when the call's partials,
+ *   float32 [P*S][B][Hq][Nq][d] and [P*S][B][Hq][Nq] each padded to 256 bytes
+ *   (P parts per split as described there), exceed FA_NOALLOC_SCRATCH_BYTES;
+ *   the decode workloads B=8, Nq=1 and 8, Nk=8192, Hq=32, Hkv=8, d=128, S=16
+ *   take about 2 and 16 MiB. FA_ERR_LAUNCH if the array's address cannot be found.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a GPU
+ * (on different streams, or from different threads) race and give undefined
+ * results; calls ordered on one stream are fine. Its contents on entry do not
+ * matter (every part writes its partial before the merge reads it).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (32u << 20)
+fa_status fa_decode_splitkv_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
+                                    float* lse, int B, int Nq, int Nk, int Hq, int Hkv, int d,
+                                    int num_splits, int causal, float scale, fa_dtype dtype, void* stream);
 
 /*
  * Split-KV attention over a paged KV cache with per-sequence lengths

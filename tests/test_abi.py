@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(11):
+    for code in range(12):
         s = lib.fa_status_str(code).decode()
         assert s and s != "unknown status"
     assert lib.fa_status_str(99).decode() == "unknown status"
@@ -98,6 +98,26 @@ def dec(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, Nq=1, Nk=64, Hq=4, H
 ])
 def test_decode_rejects_invalid_arguments(lib, kw, status):
     assert dec(lib, **kw) == status
+
+
+def dec_noalloc(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, Nq=1, Nk=64, Hq=4, Hkv=2, d=128, S=4,
+                causal=0, scale=0.1, dtype=1):
+    return lib.fa_decode_splitkv_noalloc(q, k, v, o, lse, B, Nq, Nk, Hq, Hkv, d, S, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1),
+    (dict(Nk=0), 2), (dict(Hq=5, Hkv=2), 3), (dict(d=80), 4), (dict(dtype=7), 5),
+    (dict(S=0), 6), (dict(S=_lib.FA_MAX_SPLITS + 1), 6),
+    (dict(k=MIS), 9), (dict(scale=float("nan")), 10),
+    (dict(Nk=1 << 20, Hkv=8, Hq=8, d=256), 2),
+    # partials of 16 x 8 x 32 x 64 rows of 256 floats: 256 MiB, beyond the fixed scratch
+    (dict(B=8, Nq=64, Hq=32, Hkv=32, d=256, S=16), 11),
+])
+def test_decode_noalloc_rejects_invalid_arguments(lib, kw, status):
+    """The entry point that allocates nothing validates like fa_decode_splitkv and
+    refuses a call whose partials exceed the fixed scratch, before any HIP call."""
+    assert dec_noalloc(lib, **kw) == status
 
 
 def test_python_layer_fails_loudly_without_library(tmp_path):
