@@ -42,6 +42,7 @@ PAGES_HEADLINE_TFLOPS_4X = 51.68
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_headline_traffic.json")
 KERNEL_SOURCES = ("fa_fwd_kernel.h", "fa_device.h", "fa_launch.h")
 MIN_ITERS, MIN_SECONDS = 50, 1.0
+TIMING = {"min_seconds": MIN_SECONDS}   # --min-seconds may lower it for profiler runs
 
 
 def code_only(text: str) -> str:
@@ -140,7 +141,7 @@ def timed_auto(fn, torch, warm_s, warmup=5):
     short trial run)."""
     prewarm(fn, warm_s, torch)
     trial = timed(fn, 10, 2, torch)
-    n = max(MIN_ITERS, int(math.ceil(MIN_SECONDS * 1e3 / max(trial["mean_ms"], 1e-4))))
+    n = max(MIN_ITERS, int(math.ceil(TIMING["min_seconds"] * 1e3 / max(trial["mean_ms"], 1e-4))))
     return timed(fn, min(n, 200000), warmup, torch)
 
 
@@ -345,14 +346,24 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["fwd", "headline", "fwd4096", "decode", "bwd", "all"], default="all")
+    ap.add_argument("--only", choices=["fwd", "headline", "fwd4096", "decode", "bwd", "none", "all"],
+                    default="all")
     ap.add_argument("--prewarm-s", type=float, default=1.0,
                     help="seconds of untimed launches per workload before its warmup steps")
     ap.add_argument("--no-sweep", action="store_true", help="skip the sweep over the other workloads")
     ap.add_argument("--no-kernel-trace", action="store_true",
                     help="skip the per-kernel durations (use under an outside profiler)")
+    ap.add_argument("--min-seconds", type=float, default=MIN_SECONDS,
+                    help="timed seconds per workload besides the headline (at least 50 steps); "
+                         "less for profiler runs")
+    ap.add_argument("--fwd4096-batch", type=int, default=16, metavar="B",
+                    help="batch of the N=4096 forward leg (smaller for counter runs whose totals "
+                         "would pass 2^32)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (calibrates HBM byte counters)")
+    ap.add_argument("--gemm-probe", type=int, default=0, metavar="N",
+                    help="also time torch's fp16 N x N x N matmul (the library GEMM: the MFMA rate "
+                         "and clock a tuned dense kernel sustains on this GPU)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (the units "
@@ -361,6 +372,7 @@ def main():
         return 2
     if args.no_kernel_trace:
         os.environ["FA_BENCH_NO_KERNEL_TRACE"] = "1"
+    TIMING["min_seconds"] = args.min_seconds
 
     import numpy as np
     import torch
@@ -382,6 +394,15 @@ def main():
         torch.cuda.synchronize()
         result["copy_probe_bytes"] = 2 * src.numel()   # read + write
         del src, dst
+    if args.gemm_probe:
+        n = args.gemm_probe
+        ga = torch.randn(n, n, device=dev, dtype=torch.float16)
+        gb = torch.randn(n, n, device=dev, dtype=torch.float16)
+        tg = timed(lambda i=0: ga @ gb, 40, 3, torch, 0.5)
+        result["gemm_probe"] = {"n": n, **stats_fields(tg),
+                                "tflops": round(2.0 * n ** 3 / (tg["mean_ms"] * 1e-3) / 1e12, 1)}
+        del ga, gb
+        torch.cuda.empty_cache()
     if args.only in ("fwd", "headline", "all"):
         q, k, v = upload(w, torch)
         o = torch.empty_like(q)
@@ -415,6 +436,8 @@ def main():
     if args.only in ("fwd", "fwd4096", "all"):
         # forward at N = 4096 (the 50%-of-peak target shape)
         w4 = synthetic.WORKLOADS["long_f16_4096_full"]
+        if args.fwd4096_batch != w4.B:
+            w4 = dataclasses.replace(w4, B=args.fwd4096_batch)
         q, k, v = upload(w4, torch)
         o = torch.empty_like(q)
         t4 = timed_auto(lambda i=0: attention(q, k, v, scale=w4.scale, out=o), torch, args.prewarm_s)
