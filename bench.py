@@ -104,6 +104,11 @@ def prewarm(fn, seconds, torch):
         torch.cuda.synchronize()
 
 
+def progress(msg: str) -> None:
+    """One line per finished leg on stderr (the JSON result is the only stdout line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def block_sizes(steps: int, blocks: int = 10):
     """Split `steps` into at most `blocks` nearly equal runs of consecutive steps."""
     blocks = max(1, min(blocks, steps))
@@ -283,6 +288,7 @@ def cpu_baseline_sweep(names, budget_per_s=1.5):
                 t1, units = _oracle_seconds(w, [0], heads)
             sec = t1 * (w.B * w.Hq) / units
             kind = f"extrapolated from batch 0, heads 0..{units - 1} ({t1:.2f} s) to {w.B}x{w.Hq}"
+        progress(f"oracle {name}: {sec:.3f} s ({kind})")
         if w.decode:
             rows.append({"workload": name, "us_per_step": round(sec * 1e6, 1), "sample": kind})
         else:
@@ -293,11 +299,36 @@ def cpu_baseline_sweep(names, budget_per_s=1.5):
 
 # ------------------------------------------------------------------ GPU legs
 
+# The forward's VALU work per query-key pair (score), as wave64 instructions: one FMA
+# (scale and reference max), one exponential, half a conversion to the 16-bit type (two
+# per instruction) and half a dot2 (row sum of the rounded probabilities, two per
+# instruction); bf16 adds an fp32 add (the unrounded sum for the LSE) and another half
+# dot2. Issue cost per wave64 instruction on one SIMD, from a register-only probe on
+# MI355X (exponentials and FMA-class instructions share the issue port, their times
+# add): 7.1 cycles for v_exp_f32, 2.36 for an FMA-class instruction (3.7 ns and 1.22 ns
+# at the 1.93 GHz where a 32x32x16 MFMA took its 32 cycles).
+CYC_EXP, CYC_VALU = 7.1, 2.36
+SIMDS, CLOCK_GHZ = 1024, 2.4
+
+
+def valu_bound_tflops(w) -> float:
+    """FLOP rate at which the softmax VALU work alone keeps every SIMD's issue port
+    busy at the published clock: 4 d FLOP per score, one score per lane."""
+    other = 2.0 if w.dtype == "f16" else 3.5
+    cycles_per_64_scores = CYC_EXP + other * CYC_VALU
+    scores_per_s = SIMDS * CLOCK_GHZ * 1e9 * 64 / cycles_per_64_scores
+    return scores_per_s * 4.0 * w.d / 1e12
+
+
 def fwd_row(name, w, t):
     tf = w.flops() / (t["mean_ms"] * 1e-3) / 1e12
     row = {"workload": name, **stats_fields(t), "tflops": round(tf, 2),
            "tflops_median": round(w.flops() / (t["median_ms"] * 1e-3) / 1e12, 2),
            "tflops_pages_convention": round(tf / 2, 2), "mfma_peak_frac": round(tf / PEAK_MFMA_F16, 4)}
+    vb = valu_bound_tflops(w)
+    row["valu_bound_tflops"] = round(vb, 1)
+    row["bound"] = "valu" if vb < PEAK_MFMA_F16 else "mfma"
+    row["bound_frac"] = round(tf / min(vb, PEAK_MFMA_F16), 4)
     if w.causal:   # the same time against the un-halved 4 B H N^2 d count
         row["tflops_unhalved_count"] = round(4.0 * w.B * w.Hq * w.Nq * w.Nk * w.d / (t["mean_ms"] * 1e-3) / 1e12, 2)
     return row
@@ -319,6 +350,7 @@ def sweep(args, torch, dev):
         t = timed_auto(lambda i=0: attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse),
                        torch, min(args.prewarm_s, 0.3))
         rows.append(fwd_row(name, w, t))
+        progress(f"{name}: {rows[-1]['tflops']} TFLOP/s")
         del q, k, v, o, lse
         torch.cuda.empty_cache()
     wd = synthetic.WORKLOADS["decode_bf16_nq8"]
@@ -430,6 +462,7 @@ def main():
                          "frac": round(tflops / PEAK_MFMA_F16, 4), "traffic": traffic,
                          "flop_per_launch": w.flops()},
         })
+        progress(f"headline: {result['value']} TFLOP/s")
         del q, k, v, o, lse
         torch.cuda.empty_cache()
 
@@ -442,6 +475,7 @@ def main():
         o = torch.empty_like(q)
         t4 = timed_auto(lambda i=0: attention(q, k, v, scale=w4.scale, out=o), torch, args.prewarm_s)
         result["fwd_4096"] = fwd_row(w4.name, w4, t4)
+        progress(f"fwd_4096: {result['fwd_4096']['tflops']} TFLOP/s")
         del q, k, v, o
         torch.cuda.empty_cache()
 
@@ -463,6 +497,7 @@ def main():
         result["fwd_varlen"] = {"workload": "16 packed sequences, lengths 256..2048 (seeded), Hq=Hkv=32, d=128, f16",
                                 "tokens": tot, **stats_fields(tv),
                                 "tflops": round(fl / (tv["mean_ms"] * 1e-3) / 1e12, 2)}
+        progress(f"fwd_varlen: {result['fwd_varlen']['tflops']} TFLOP/s")
         del qv, kv_, vv_, ov
         torch.cuda.empty_cache()
 
@@ -500,6 +535,7 @@ def main():
                             "copy_frac": round(kv_bytes / (msd * 1e-3) / 1e9 / copy_gbps, 4),
                             "kv_sets_rotated": len(sets),
                             "kernels_us": kernel_times(dstep, 40, torch)}
+        progress(f"decode: {result['decode']['us_per_step']} us/step")
         # the same step over a paged cache: 256-key pages in a scrambled block table
         from exact_tiled_attention_21_amd import decode_paged
         ps, mp = 256, wd.Nk // 256
@@ -556,11 +592,13 @@ def main():
                 "tflops_executed": round(tb * 3.5 / 2.5, 2),
                 "mfma_peak_frac": round(tb / PEAK_MFMA_F16, 4),
                 "kernels_us": kernel_times(bstep, 10, torch)}
+            progress(f"{wb.name}: {tb:.1f} TFLOP/s (pages' convention)")
             del q, k, v, do, o, lse, ws, dq, dk, dv
             torch.cuda.empty_cache()
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w)
+        progress("cpu baseline (headline) done")
         if args.only == "all":
             names = (["tiny_f16_128"] + [n for n in synthetic.WORKLOADS if n.startswith("long_")]
                      + [n for n in synthetic.WORKLOADS if n.startswith("gqa_")] + ["decode_bf16_nq1"])
