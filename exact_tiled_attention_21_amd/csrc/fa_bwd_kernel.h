@@ -41,6 +41,8 @@ template <int D> struct BwdCfg {
   static constexpr int TILE = BT * D * 2;           // bytes of one [32][D] tile
   static constexpr int BQ = 64;                     // query rows per step of the dK/dV pass
   static constexpr int TILEQ = BQ * D * 2;
+  static constexpr int STW = 256;                   // floats of one wave's copy of a step's row statistics
+  static_assert(STW * 4 == 64 * 16 && 2 * BQ <= STW, "one 16-byte DMA per lane fills a copy");
 };
 
 // DMA of [ROWS][D] row tiles (row pitch `pitch` bytes) into swizzled LDS. Piece
@@ -78,7 +80,7 @@ template <int D, int ROWS> struct BwdDma {
 };
 
 // Two LDS stages of two row tiles each (Q and dO, or K and V), and for the
-// dK/dV pass the row statistics of each stage.
+// dK/dV pass the row statistics of each stage (one copy per wave).
 struct BwdLds {
   char* x[2];
   char* y[2];
@@ -230,21 +232,23 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
   }
 
   // Q and dO rows t*64 .. of query head hi of the group into one stage, and
-  // their statistics: the log2 LSE of the 64 rows, then their D (lanes 0..15
-  // and 16..31 of wave 0 move 16 bytes each)
-  __device__ __forceinline__ void fetch(int hi, int t, char* ql, char* ol, float* stl) const {
+  // their statistics into this wave's copy: the log2 LSE of the 64 rows, then
+  // their D (lanes 0..15 and 16..31 move 16 bytes each, lanes 32..63 repeat
+  // them). Branch-free, so that the DMA can sit among the MFMAs: when `live`
+  // is false every range is empty, nothing is read and the stage is zeroed.
+  __device__ __forceinline__ void fetch(int hi, int t, char* ql, char* ol, float* stl, bool live) const {
     const size_t off = ((sq.q_row0 + t * C::BQ) * a.Hq + g * a.group + hi) * D * 2;
-    const int64_t valid = static_cast<int64_t>(sq.nq - t * C::BQ - 1) * qpitch + D * 2;
+    const int64_t valid = live ? static_cast<int64_t>(sq.nq - t * C::BQ - 1) * qpitch + D * 2 : 0;
     dma.issue(reinterpret_cast<const char*>(a.q) + off, valid, ql);
     dma.issue(reinterpret_cast<const char*>(a.dout) + off, valid, ol);
-    if (wave == 0 && lane < 32) {
+    {
       const uint32_t lse_off = static_cast<uint32_t>(reinterpret_cast<const char*>(a.lse2) -
                                                      reinterpret_cast<const char*>(a.dsum));
       const uint32_t row0 = ((b * a.Hq + g * a.group + hi) * nqp + t * C::BQ + 4 * (lane & 15)) * 4;
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          a.dsum, 0, lse_off + static_cast<uint32_t>(a.B * a.Hq * nqp) * 4, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)stl, 16,
-                                               (lane < 16 ? lse_off : 0u) + row0, 0, 0, 0);
+          a.dsum, 0, live ? lse_off + static_cast<uint32_t>(a.B * a.Hq * nqp) * 4 : 0u, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(stl + wave * C::STW), 16,
+                                               ((lane & 31) < 16 ? lse_off : 0u) + row0, 0, 0, 0);
     }
   }
 
@@ -304,7 +308,13 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
   __device__ __forceinline__ V8 sd_frag(const char* qt, const char* ot, int m) const {
     return row_frag<D, V8>(((m & 1) ? ot : qt) + (m / (2 * C::NS)) * C::TILE, (m / 2) % C::NS, lane);
   }
-  __device__ __forceinline__ void sdp(const char* qt, const char* ot, f32x16 (&s)[2], f32x16 (&dp)[2]) const {
+  // The next tile's DMA (`hook`) goes out after MFMA kFetchAt, one instruction
+  // per following MFMA. At d <= 64, whose two waves per SIMD leave no
+  // registers for its addresses to stay live that long, the caller issues it
+  // before the step's first MFMA instead (kFetchAt < 0: no hook call here).
+  static constexpr int kFetchAt = D <= 64 ? -1 : 4;
+  template <typename Hook>
+  __device__ __forceinline__ void sdp(const char* qt, const char* ot, f32x16 (&s)[2], f32x16 (&dp)[2], Hook hook) const {
     s[0] = s[1] = dp[0] = dp[1] = f32x16{};
     V8 fr[kPre];
 #pragma unroll
@@ -315,29 +325,31 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
       if (m & 1) dp[h2] = E::mfma(fr[m % kPre], vf[i], dp[h2]);
       else s[h2] = E::mfma(fr[m % kPre], kf[i], s[h2]);
       if (m + kPre < kSdMf) fr[m % kPre] = sd_frag(qt, ot, m + kPre);
+      if (m == kFetchAt) hook();
     }
     __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
 #pragma unroll
     for (int m = 0; m < kSdMf; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (m + kPre < kSdMf) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (kFetchAt >= 0 && m >= kFetchAt && m < kFetchAt + 2 * BwdDma<D, C::BQ>::C::NDMA + 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
     }
   }
 
   // Tile t (64 query rows) of query head hi, in stage ST: S = Q K^T and
   // dP = dO V^T for both 32-row halves first, so that the exponentials of one
   // half can overlap the products of the other. The next tile (in head-major
-  // order) is fetched first.
+  // order; none after the last) is fetched into the other stage meanwhile.
   template <int ST, bool MASK>
   __device__ __forceinline__ void step(int hi, int t, const BwdLds& lds) {
-    {
-      int hn = hi, tn = t + 1;
-      if (tn == t1) {
-        hn = hi + 1;
-        tn = t0;
-      }
-      if (hn < a.group) fetch(hn, tn, lds.x[ST ^ 1], lds.y[ST ^ 1], lds.st[ST ^ 1]);
+    int hn = hi, tn = t + 1;
+    if (tn == t1) {
+      hn = hi + 1;
+      tn = t0;
     }
+    const bool live = hn < a.group;
+    hn = live ? hn : 0;   // keeps the (unused) address inside the tensors
+    if (kFetchAt < 0 && live) fetch(hn, tn, lds.x[ST ^ 1], lds.y[ST ^ 1], lds.st[ST ^ 1], true);
     const char* qt = lds.x[ST];
     const char* ot = lds.y[ST];
     // statistics of rows 32 h2 + 8 gq + 4 hh + 0..3, read before the pinned
@@ -347,12 +359,12 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        l4[h2][gq] = *reinterpret_cast<const f32x4*>(lds.st[ST] + h2 * C::BT + 8 * gq + 4 * hh);
-        d4[h2][gq] = *reinterpret_cast<const f32x4*>(lds.st[ST] + C::BQ + h2 * C::BT + 8 * gq + 4 * hh);
+        l4[h2][gq] = *reinterpret_cast<const f32x4*>(lds.st[ST] + wave * C::STW + h2 * C::BT + 8 * gq + 4 * hh);
+        d4[h2][gq] = *reinterpret_cast<const f32x4*>(lds.st[ST] + wave * C::STW + C::BQ + h2 * C::BT + 8 * gq + 4 * hh);
       }
     __builtin_amdgcn_sched_barrier(0);
     f32x16 s[2], dp[2];
-    sdp(qt, ot, s, dp);
+    sdp(qt, ot, s, dp, [&] { fetch(hn, tn, lds.x[ST ^ 1], lds.y[ST ^ 1], lds.st[ST ^ 1], live); });
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
       half<MASK>(t * C::BQ + h2 * C::BT, qt + h2 * C::TILE, ot + h2 * C::TILE, l4[h2], d4[h2], s[h2], dp[h2]);
@@ -377,13 +389,13 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
     }
   }
 
-  // dV, and dK = scale (dK^T)^T, rounded to the element type
-  __device__ __forceinline__ void finish() const {
-    if (key >= sq.nk) return;
-    const size_t row = ((sq.k_row0 + key) * a.Hkv + g) * D;
-    T* dvp = reinterpret_cast<T*>(a.dv) + row;
-    T* dkp = reinterpret_cast<T*>(a.dk) + row;
+  // dV, and dK = scale (dK^T)^T, rounded to the element type. The wave's 32
+  // key rows of each go through LDS (`stage`: two swizzled [32][D] tiles of
+  // this wave alone), so that the global stores write whole rows, 16 bytes per
+  // lane with consecutive lanes adjacent.
+  __device__ __forceinline__ void finish(char* stage) const {
     typedef T T4 __attribute__((ext_vector_type(4)));
+    const int ln32 = lane & 31;
 #pragma unroll
     for (int cb = 0; cb < C::NCB; ++cb)
 #pragma unroll
@@ -394,9 +406,25 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
           wv[e] = static_cast<T>(dvt[cb][4 * gr + e]);
           wk[e] = static_cast<T>(dkt[cb][4 * gr + e] * a.scale);
         }
-        *reinterpret_cast<T4*>(dvp + 32 * cb + 8 * gr + 4 * hh) = wv;
-        *reinterpret_cast<T4*>(dkp + 32 * cb + 8 * gr + 4 * hh) = wk;
+        *reinterpret_cast<T4*>(stage + Swz<D>::off(ln32, 4 * cb + gr) + 8 * hh) = wv;
+        *reinterpret_cast<T4*>(stage + C::TILE + Swz<D>::off(ln32, 4 * cb + gr) + 8 * hh) = wk;
       }
+    wave_lds_sync();
+    constexpr int CPR = D / 8;   // 16-byte chunks per row
+    T* const dvb = reinterpret_cast<T*>(a.dv) + ((sq.k_row0 + k0w) * a.Hkv + g) * D;
+    T* const dkb = reinterpret_cast<T*>(a.dk) + ((sq.k_row0 + k0w) * a.Hkv + g) * D;
+#pragma unroll
+    for (int i = 0; i < C::BT * CPR / 64; ++i) {
+      const uint32_t c = 64 * i + lane;
+      const uint32_t r = c / CPR, x = c % CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + Swz<D>::off(r, x));
+      const u32x4 k = *reinterpret_cast<const u32x4*>(stage + C::TILE + Swz<D>::off(r, x));
+      if (k0w + static_cast<int>(r) < sq.nk) {
+        const size_t o = static_cast<size_t>(r) * a.Hkv * D + 8 * x;
+        *reinterpret_cast<u32x4*>(dvb + o) = v;
+        *reinterpret_cast<u32x4*>(dkb + o) = k;
+      }
+    }
   }
 };
 
@@ -408,8 +436,8 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char q_lds1[C::TILEQ];
   __shared__ __attribute__((aligned(1024))) char o_lds0[C::TILEQ];
   __shared__ __attribute__((aligned(1024))) char o_lds1[C::TILEQ];
-  __shared__ __attribute__((aligned(16))) float st_lds0[2 * C::BQ];
-  __shared__ __attribute__((aligned(16))) float st_lds1[2 * C::BQ];
+  __shared__ __attribute__((aligned(16))) float st_lds0[C::NW * C::STW];
+  __shared__ __attribute__((aligned(16))) float st_lds1[C::NW * C::STW];
 
   const int nkt = (a.Nk + C::WROWS - 1) / C::WROWS;
   int kt, gb;
@@ -436,7 +464,7 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
     u0 = min(w.t1, max(w.t0, ua > 0 ? (ua + C::BQ - 1) / C::BQ : 0));
     u1 = max(u0, min(w.t1, ub >= 0 ? (ub + 1) / C::BQ : 0));
   }
-  if (w.t0 < w.t1) w.fetch(0, w.t0, lds.x[0], lds.y[0], lds.st[0]);
+  w.fetch(0, w.t0, lds.x[0], lds.y[0], lds.st[0], w.t0 < w.t1);
   __syncthreads();
   int n = 0;
   for (int hi = 0; hi < a.group && w.t0 < w.t1; ++hi) {
@@ -444,7 +472,12 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
     w.template run<false>(hi, u0, u1, n, lds);
     w.template run<true>(hi, u1, w.t1, n, lds);
   }
-  w.finish();
+  __syncthreads();   // every wave is done with the last tile before the stages hold results
+  {
+    static_assert(C::NW == 4 && 2 * C::TILE <= C::TILEQ, "one stage buffer per wave holds its dV and dK rows");
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    w.finish(wv == 0 ? q_lds0 : wv == 1 ? q_lds1 : wv == 2 ? o_lds0 : o_lds1);
+  }
 }
 
 // ---------------------------------------------------------------- dQ
