@@ -38,6 +38,11 @@ template <int D> struct BwdCfg {
   static constexpr int WROWS = NW * BT;             // rows a workgroup owns
   static constexpr int NS = D / 16;                 // 16-wide d slices
   static constexpr int NCB = D / 32;                // 32-wide d blocks
+  // dK/dV workgroups per key block, each owning NCBO of the d blocks of dK and
+  // dV (S and dP still contract over all of d): at d = 256 one wave's dK, dV,
+  // K and V alone would take 384 of its 512 registers
+  static constexpr int DSPLIT = D > 192 ? 2 : 1;
+  static constexpr int NCBO = NCB / DSPLIT;
   static constexpr int TILE = BT * D * 2;           // bytes of one [32][D] tile
   static constexpr int BQ = 64;                     // query rows per step of the dK/dV pass
   static constexpr int TILEQ = BQ * D * 2;
@@ -187,15 +192,16 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
   const BwdSeq& sq;
   int lane, wave, hh;
   int b, g, key, k0w, diag;
+  int cb0;                // first d block of dK and dV this workgroup owns
   int nqt, t0, t1, nqp;   // query tiles [t0, t1) see some key of the workgroup
   int qlo, qspan;         // rows q that see this lane's key: 0 <= q - qlo <= qspan (unsigned)
   uint32_t qpitch;
   V8 kf[C::NS], vf[C::NS];          // this lane's key row of K and V (B operands)
-  f32x16 dvt[C::NCB], dkt[C::NCB];  // dV^T and dK^T, [d][key]
+  f32x16 dvt[C::NCBO], dkt[C::NCBO];  // dV^T and dK^T, [d][key], d blocks cb0 ..
   BwdDma<D, C::BQ> dma;
 
-  __device__ __forceinline__ DkdvWave(const BwdArgs& args, const BwdSeq& seq, int b_, int g_, int k0)
-      : a(args), sq(seq), b(b_), g(g_) {
+  __device__ __forceinline__ DkdvWave(const BwdArgs& args, const BwdSeq& seq, int b_, int g_, int k0, int dh)
+      : a(args), sq(seq), b(b_), g(g_), cb0(dh * C::NCBO) {
     lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     hh = lane >> 5;
@@ -224,7 +230,7 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
       vf[s] = key < sq.nk ? *reinterpret_cast<const V8*>(vp + 16 * s) : V8{};
     }
 #pragma unroll
-    for (int cb = 0; cb < C::NCB; ++cb) {
+    for (int cb = 0; cb < C::NCBO; ++cb) {
       dvt[cb] = f32x16{};
       dkt[cb] = f32x16{};
     }
@@ -273,14 +279,14 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
     }
     const V8 pf[2] = {to_v8<BF16>(p, 0), to_v8<BF16>(p, 8)};
     const V8 dsf[2] = {to_v8<BF16>(ds, 0), to_v8<BF16>(ds, 8)};
-    // MFMA m: key slice u = m / (2 NCB), d block cb = (m / 2) % NCB, dV (even m,
-    // dO^T fragment) or dK (odd m, Q^T fragment); fragments kTrPre MFMAs ahead
+    // MFMA m: key slice u = m / (2 NCBO), d block cb0 + (m / 2) % NCBO, dV (even
+    // m, dO^T fragment) or dK (odd m, Q^T fragment); fragments kTrPre MFMAs ahead
     V8 fr[kTrPre];
 #pragma unroll
     for (int m = 0; m < kTrPre; ++m) fr[m] = tr_frag(qt, ot, m);
 #pragma unroll
     for (int m = 0; m < kTrMf; ++m) {
-      const int u = m / (2 * C::NCB), cb = (m / 2) % C::NCB;
+      const int u = m / (2 * C::NCBO), cb = (m / 2) % C::NCBO;
       if (m & 1) dkt[cb] = E::mfma(fr[m % kTrPre], dsf[u], dkt[cb]);
       else dvt[cb] = E::mfma(fr[m % kTrPre], pf[u], dvt[cb]);
       if (m + kTrPre < kTrMf) fr[m % kTrPre] = tr_frag(qt, ot, m + kTrPre);
@@ -292,10 +298,10 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
       if (m + kTrPre < kTrMf) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   }
-  static constexpr int kTrMf = 4 * C::NCB;
+  static constexpr int kTrMf = 4 * C::NCBO;
   static constexpr int kTrPre = 3;
   __device__ __forceinline__ V8 tr_frag(const char* qt, const char* ot, int m) const {
-    return v_frag<D, V8>((m & 1) ? qt : ot, (m / 2) % C::NCB, m / (2 * C::NCB), lane);
+    return v_frag<D, V8>((m & 1) ? qt : ot, cb0 + (m / 2) % C::NCBO, m / (2 * C::NCBO), lane);
   }
 
   // S = Q K^T and dP = dO V^T for both 32-row halves of a tile: MFMA m takes
@@ -389,15 +395,16 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
     }
   }
 
-  // dV, and dK = scale (dK^T)^T, rounded to the element type. The wave's 32
-  // key rows of each go through LDS (`stage`: two swizzled [32][D] tiles of
-  // this wave alone), so that the global stores write whole rows, 16 bytes per
-  // lane with consecutive lanes adjacent.
+  // dV, and dK = scale (dK^T)^T, rounded to the element type (the workgroup's
+  // d blocks of them). The wave's 32 key rows of each go through LDS (`stage`:
+  // two swizzled [32][D] tiles of this wave alone), so that the global stores
+  // write whole rows (half rows at d = 256), 16 bytes per lane with consecutive
+  // lanes adjacent.
   __device__ __forceinline__ void finish(char* stage) const {
     typedef T T4 __attribute__((ext_vector_type(4)));
     const int ln32 = lane & 31;
 #pragma unroll
-    for (int cb = 0; cb < C::NCB; ++cb)
+    for (int cb = 0; cb < C::NCBO; ++cb)
 #pragma unroll
       for (int gr = 0; gr < 4; ++gr) {
         T4 wv, wk;
@@ -406,17 +413,17 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
           wv[e] = static_cast<T>(dvt[cb][4 * gr + e]);
           wk[e] = static_cast<T>(dkt[cb][4 * gr + e] * a.scale);
         }
-        *reinterpret_cast<T4*>(stage + Swz<D>::off(ln32, 4 * cb + gr) + 8 * hh) = wv;
-        *reinterpret_cast<T4*>(stage + C::TILE + Swz<D>::off(ln32, 4 * cb + gr) + 8 * hh) = wk;
+        *reinterpret_cast<T4*>(stage + Swz<D>::off(ln32, 4 * (cb0 + cb) + gr) + 8 * hh) = wv;
+        *reinterpret_cast<T4*>(stage + C::TILE + Swz<D>::off(ln32, 4 * (cb0 + cb) + gr) + 8 * hh) = wk;
       }
     wave_lds_sync();
-    constexpr int CPR = D / 8;   // 16-byte chunks per row
+    constexpr int CPR = 4 * C::NCBO;   // 16-byte chunks per row that this workgroup owns
     T* const dvb = reinterpret_cast<T*>(a.dv) + ((sq.k_row0 + k0w) * a.Hkv + g) * D;
     T* const dkb = reinterpret_cast<T*>(a.dk) + ((sq.k_row0 + k0w) * a.Hkv + g) * D;
 #pragma unroll
     for (int i = 0; i < C::BT * CPR / 64; ++i) {
       const uint32_t c = 64 * i + lane;
-      const uint32_t r = c / CPR, x = c % CPR;
+      const uint32_t r = c / CPR, x = 4 * cb0 + c % CPR;
       const u32x4 v = *reinterpret_cast<const u32x4*>(stage + Swz<D>::off(r, x));
       const u32x4 k = *reinterpret_cast<const u32x4*>(stage + C::TILE + Swz<D>::off(r, x));
       if (k0w + static_cast<int>(r) < sq.nk) {
@@ -452,7 +459,7 @@ void fa_bwd_dkdv_kernel(const BwdArgs a) {
   const int k0 = kt * C::WROWS;
   const BwdSeq sq(a, b);
   if (k0 >= sq.nk) return;   // a packed sequence shorter than the grid: uniform, before any barrier
-  DkdvWave<D, BF16, BAND> w(a, sq, b, g, k0);
+  DkdvWave<D, BF16, BAND> w(a, sq, b, g, k0, C::DSPLIT > 1 ? static_cast<int>(blockIdx.y) : 0);
   const BwdLds lds{{q_lds0, q_lds1}, {o_lds0, o_lds1}, {st_lds0, st_lds1}};
 
   // tiles [u0, u1) hold only rows that see every key of the workgroup; the
@@ -697,7 +704,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, bool bf16, bool band, hipStream_t stre
     else fa_bwd_pre_kernel<D, false><<<grid, 256, 0, stream>>>(a);
   }
   const dim3 block(C::THREADS);
-  const dim3 grid_kv(static_cast<unsigned>((a.Nk + C::WROWS - 1) / C::WROWS) * a.Hkv * a.B);
+  const dim3 grid_kv(static_cast<unsigned>((a.Nk + C::WROWS - 1) / C::WROWS) * a.Hkv * a.B, C::DSPLIT);
   const dim3 grid_q(static_cast<unsigned>((a.Nq + C::WROWS - 1) / C::WROWS) * a.Hq * a.B);
   if (bf16) {
     if (band) {
