@@ -14,16 +14,17 @@
 // the parts of a sequence read one dense window of the cache at a time (all
 // parts step through neighbouring tiles together), which keeps the DRAM pages
 // open: with contiguous chunks every part streams its own region. One
-// single-wave workgroup per (part, KV head, batch[, row block]); the query rows
+// single-wave workgroup per (part, KV head, batch[, row block]) (two waves at
+// d = 256, splitting the tile's loads and O's columns); the query rows
 // of the whole GQA group (Hq/Hkv heads x Nq positions, at most 32 per row block)
 // share the part's K/V, which is therefore read from HBM once. The wave loads
 // each tile with fully coalesced, non-temporal 16-byte loads into registers
-// (one tile ahead: about 16 MiB in flight chip-wide is enough for the HBM rate,
+// (one tile ahead, except at d = 192: about 16 MiB in flight chip-wide is enough for the HBM rate,
 // more only thins out the DRAM locality), stages it through its own swizzled
 // LDS tiles (K for the A operand, V for the transposing read), and writes one
 // normalised fp32 partial and its log-sum-exp per row; the combine kernel
-// merges the partials. No barriers: up to four such waves share a CU, one per
-// SIMD.
+// merges the partials. No barriers between single waves: up to four share a CU,
+// one per SIMD.
 //
 // Paged cache ("flash-attention-v100" README, flash_attn_with_kvcache: a block
 // table maps each sequence's logical key blocks to pages of a shared pool, and
@@ -48,6 +49,16 @@ template <int D> struct DecCfg {
   static constexpr int NCB = D / 32;              // 32-wide d blocks of O^T
   static constexpr int CPR = D / 8;               // 16-byte chunks per row
   static constexpr int NCH = BC * CPR / 64;       // 16-byte chunks per lane per tensor per tile
+  // waves per workgroup: at d = 256 two waves share the tile (each loads half of
+  // it) and each accumulates half of O's d blocks; both compute all the scores
+  static constexpr int NWV = D > 192 ? 2 : 1;
+  static constexpr int NCBO = NCB / NWV;          // d blocks of O^T per wave
+  static constexpr int NCHW = NCH / NWV;          // chunks per lane per tensor per tile per wave
+  // the next tile's loads go out before the current tile's products when a
+  // wave's share of a tile is at most 8 chunks per tensor; more (d = 192), live
+  // across those products, would spill
+  static constexpr bool AHEAD = NCHW <= 8;
+  static_assert(NCB % NWV == 0 && NCH % NWV == 0, "the waves split O and the tile evenly");
   static constexpr int TILE = BC * D * 2;         // bytes of one K or V tile
 };
 
@@ -61,17 +72,17 @@ template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
   using E = Elem<BF16>;
   using T = typename E::T;
   using V8 = typename E::V8;
-  typedef u32x4 Stage[C::NCH];
+  typedef u32x4 Stage[C::NCHW];
 
   const DecodeArgs& a;
-  int lane, hh;
+  int lane, hh, wv;             // wv: this wave's index in the workgroup
   bool rvalid;
   int b, g, L;                  // batch, KV head, keys of this sequence
   int ri, rhq, diag, i_first, k_hi, ntile;
   int part, nparts;             // this part's index and the number of parts (tile stride)
   float sl2;
   V8 qf[C::NS];
-  f32x16 oacc[C::NCB];
+  f32x16 oacc[C::NCBO];         // O^T, d blocks wv NCBO ..
   float m_run, l_part;
   const char* kg;
   const char* vg;
@@ -84,6 +95,7 @@ template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
       : a(args), b(b_), g(g_) {
     lane = threadIdx.x & 63;
     hh = lane >> 5;
+    wv = C::NWV > 1 ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)) : 0;
     const int R = a.group * a.Nq;               // rows of this KV head group
     L = a.Nk;
     if (PAGED) L = min(max(a.seqlens[b], 0), a.max_pages * a.page_size);
@@ -137,7 +149,7 @@ template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
     vb0 = vrow0 * (D * 2) + 8 * (vj & 1);
     vb1 = vrow1 * (D * 2) + 8 * (vj & 1);
 #pragma unroll
-    for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] = f32x16{};
+    for (int cb = 0; cb < C::NCBO; ++cb) oacc[cb] = f32x16{};
     m_run = kNegInf;
     l_part = 0.f;
   }
@@ -170,10 +182,10 @@ template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(vg + off), 0, nrec, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < C::NCH; ++i) {
-      const uint32_t o = goff_of(i);
-      ks[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kNonTemporal));
-      vs[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, kNonTemporal));
+    for (int j = 0; j < C::NCHW; ++j) {
+      const uint32_t o = goff_of(wv * C::NCHW + j);
+      ks[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kNonTemporal));
+      vs[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, kNonTemporal));
     }
   }
   // piece i of a tile is 16-byte chunk c = lane + 64 i of the tile: row c / CPR, chunk c % CPR
@@ -183,14 +195,15 @@ template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
     const uint32_t c = lane + 64 * i;
     return (c / C::CPR) * rowbytes + (c % C::CPR) * 16;
   }
-  // registers -> the wave's swizzled LDS tiles
+  // registers -> the workgroup's swizzled LDS tiles (this wave's pieces)
   __device__ __forceinline__ void stage(const Stage& ks, const Stage& vs, char* kt, char* vt) const {
 #pragma unroll
-    for (int i = 0; i < C::NCH; ++i) {
+    for (int j = 0; j < C::NCHW; ++j) {
+      const int i = wv * C::NCHW + j;
       const uint32_t c = lane + 64 * i;
       const uint32_t o = Swz<D>::off(c / C::CPR, c % C::CPR);
-      *reinterpret_cast<u32x4*>(kt + o) = ks[i];
-      *reinterpret_cast<u32x4*>(vt + o) = vs[i];
+      *reinterpret_cast<u32x4*>(kt + o) = ks[j];
+      *reinterpret_cast<u32x4*>(vt + o) = vs[j];
     }
   }
   __device__ __forceinline__ V8 kfrag(const char* kt, int s) const {
@@ -228,7 +241,7 @@ template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
       const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m_run - m_new);
       l_part *= alpha;
 #pragma unroll
-      for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] *= alpha;
+      for (int cb = 0; cb < C::NCBO; ++cb) oacc[cb] *= alpha;
       m_run = m_new;
     }
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
@@ -246,7 +259,7 @@ template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
     for (int tt = 0; tt < 2; ++tt) {
       const V8 pf = to_v8<BF16>(p, 8 * tt);
 #pragma unroll
-      for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] = E::mfma(vfrag(vt, cb, tt), pf, oacc[cb]);
+      for (int cb = 0; cb < C::NCBO; ++cb) oacc[cb] = E::mfma(vfrag(vt, wv * C::NCBO + cb, tt), pf, oacc[cb]);
     }
   }
   __device__ __forceinline__ void tile_any(int t, const char* kt, const char* vt) {
@@ -256,8 +269,15 @@ template <int D, bool BF16, bool CAUSAL, bool PAGED> struct DecWave {
   }
 };
 
+// LDS hand-over between the workgroup's waves: the wave's own when it is alone
+template <int NWV>
+__device__ __forceinline__ void dec_lds_sync() {
+  if (NWV > 1) __syncthreads();
+  else wave_lds_sync();
+}
+
 template <int D, bool BF16, bool CAUSAL, bool PAGED>
-__global__ __launch_bounds__(64) void fa_decode_split_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(64 * DecCfg<D>::NWV) void fa_decode_split_kernel(const DecodeArgs a) {
   using C = DecCfg<D>;
   using W = DecWave<D, BF16, CAUSAL, PAGED>;
   __shared__ __attribute__((aligned(1024))) char kt[C::TILE];
@@ -274,16 +294,18 @@ __global__ __launch_bounds__(64) void fa_decode_split_kernel(const DecodeArgs a)
   W w(a, part, g, rb, b);
 
   // tiles t of this part: the loads of tile t + 1 are issued once tile t sits in
-  // LDS, so they overlap tile t's products; loads past the end read zeros, so
-  // each tile's wait covers exactly its own loads
+  // LDS, so they overlap tile t's products (d = 192 loads each tile right before
+  // staging it and relies on the other waves of the CU);
+  // loads past the end read zeros, so each tile's wait covers exactly its own loads
   typename W::Stage ks, vs;
-  w.load(0, ks, vs);
+  if (C::AHEAD) w.load(0, ks, vs);
   for (int t = 0; t < w.ntile; ++t) {
+    if (!C::AHEAD) w.load(t, ks, vs);
     w.stage(ks, vs, kt, vt);
-    wave_lds_sync();
-    w.load(t + 1, ks, vs);
+    dec_lds_sync<C::NWV>();
+    if (C::AHEAD) w.load(t + 1, ks, vs);
     w.tile_any(t, kt, vt);
-    wave_lds_sync();
+    dec_lds_sync<C::NWV>();
   }
 
   // normalised partial and its log2-sum-exp; a part with no visible key
@@ -294,15 +316,15 @@ __global__ __launch_bounds__(64) void fa_decode_split_kernel(const DecodeArgs a)
   const size_t prow = ((static_cast<size_t>(part) * a.B + b) * a.Hq + w.rhq) * a.Nq + w.ri;
   float* po = a.part_o + prow * D;
 #pragma unroll
-  for (int cb = 0; cb < C::NCB; ++cb)
+  for (int cb = 0; cb < C::NCBO; ++cb)
 #pragma unroll
     for (int gr = 0; gr < 4; ++gr) {
       f32x4 o4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) o4[e] = w.oacc[cb][4 * gr + e] * inv;
-      *reinterpret_cast<f32x4*>(po + 32 * cb + 8 * gr + 4 * w.hh) = o4;
+      *reinterpret_cast<f32x4*>(po + 32 * (w.wv * C::NCBO + cb) + 8 * gr + 4 * w.hh) = o4;
     }
-  if (w.hh == 0) a.part_lse[prow] = l > 0.f ? w.m_run + __log2f(l) : kNegInf;
+  if (w.hh == 0 && w.wv == 0) a.part_lse[prow] = l > 0.f ? w.m_run + __log2f(l) : kNegInf;
 }
 
 // One row of the output per D/4 threads: O = sum_s w_s O_s with
@@ -371,13 +393,14 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(const DecodeArgs
 
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, bool bf16, bool causal, hipStream_t stream) {
+  using C = DecCfg<D>;
   const dim3 grid1(a.B, a.splits, a.Hkv * a.row_blocks);   // a.splits = all parts
   (void)hipGetLastError();   // start from a clean error state
   const bool paged = a.block_table != nullptr;
 #define FA_DEC_SPLIT(BF, CA)                                                     \
   do {                                                                           \
-    if (paged) fa_decode_split_kernel<D, BF, CA, true><<<grid1, 64, 0, stream>>>(a); \
-    else fa_decode_split_kernel<D, BF, CA, false><<<grid1, 64, 0, stream>>>(a);      \
+    if (paged) fa_decode_split_kernel<D, BF, CA, true><<<grid1, 64 * C::NWV, 0, stream>>>(a); \
+    else fa_decode_split_kernel<D, BF, CA, false><<<grid1, 64 * C::NWV, 0, stream>>>(a);      \
   } while (0)
   if (bf16) {
     if (causal) FA_DEC_SPLIT(true, true);
