@@ -192,7 +192,7 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
   const BwdSeq& sq;
   int lane, wave, hh;
   int b, g, key, k0w, diag;
-  int cb0;                // first d block of dK and dV this workgroup owns
+  int cb0_;               // first d block of dK and dV this workgroup owns (see cb0)
   int nqt, t0, t1, nqp;   // query tiles [t0, t1) see some key of the workgroup
   int qlo, qspan;         // rows q that see this lane's key: 0 <= q - qlo <= qspan (unsigned)
   uint32_t qpitch;
@@ -201,7 +201,7 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
   BwdDma<D, C::BQ> dma;
 
   __device__ __forceinline__ DkdvWave(const BwdArgs& args, const BwdSeq& seq, int b_, int g_, int k0, int dh)
-      : a(args), sq(seq), b(b_), g(g_), cb0(dh * C::NCBO) {
+      : a(args), sq(seq), b(b_), g(g_), cb0_(dh * C::NCBO) {
     lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     hh = lane >> 5;
@@ -298,10 +298,12 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
       if (m + kTrPre < kTrMf) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   }
+  // a compile-time 0 unless dK and dV are split over workgroups
+  __device__ __forceinline__ int cb0() const { return C::DSPLIT > 1 ? cb0_ : 0; }
   static constexpr int kTrMf = 4 * C::NCBO;
   static constexpr int kTrPre = 3;
   __device__ __forceinline__ V8 tr_frag(const char* qt, const char* ot, int m) const {
-    return v_frag<D, V8>((m & 1) ? qt : ot, cb0 + (m / 2) % C::NCBO, m / (2 * C::NCBO), lane);
+    return v_frag<D, V8>((m & 1) ? qt : ot, cb0() + (m / 2) % C::NCBO, m / (2 * C::NCBO), lane);
   }
 
   // S = Q K^T and dP = dO V^T for both 32-row halves of a tile: MFMA m takes
@@ -359,21 +361,29 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
     const char* qt = lds.x[ST];
     const char* ot = lds.y[ST];
     // statistics of rows 32 h2 + 8 gq + 4 hh + 0..3, read before the pinned
-    // phases so that only fragment reads are left for them to order
+    // phases so that only fragment reads are left for them to order (at d <= 64,
+    // whose two waves per SIMD have no room for both halves' at once, each
+    // half's right before its products)
     f32x4 l4[2][4], d4[2][4];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+    auto stats = [&](int h2) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         l4[h2][gq] = *reinterpret_cast<const f32x4*>(lds.st[ST] + wave * C::STW + h2 * C::BT + 8 * gq + 4 * hh);
         d4[h2][gq] = *reinterpret_cast<const f32x4*>(lds.st[ST] + wave * C::STW + C::BQ + h2 * C::BT + 8 * gq + 4 * hh);
       }
+    };
+    if (D > 64) {
+      stats(0);
+      stats(1);
+    }
     __builtin_amdgcn_sched_barrier(0);
     f32x16 s[2], dp[2];
     sdp(qt, ot, s, dp, [&] { fetch(hn, tn, lds.x[ST ^ 1], lds.y[ST ^ 1], lds.st[ST ^ 1], live); });
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+    for (int h2 = 0; h2 < 2; ++h2) {
+      if (D <= 64) stats(h2);
       half<MASK>(t * C::BQ + h2 * C::BT, qt + h2 * C::TILE, ot + h2 * C::TILE, l4[h2], d4[h2], s[h2], dp[h2]);
+    }
     __syncthreads();
   }
 
@@ -413,8 +423,8 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
           wv[e] = static_cast<T>(dvt[cb][4 * gr + e]);
           wk[e] = static_cast<T>(dkt[cb][4 * gr + e] * a.scale);
         }
-        *reinterpret_cast<T4*>(stage + Swz<D>::off(ln32, 4 * (cb0 + cb) + gr) + 8 * hh) = wv;
-        *reinterpret_cast<T4*>(stage + C::TILE + Swz<D>::off(ln32, 4 * (cb0 + cb) + gr) + 8 * hh) = wk;
+        *reinterpret_cast<T4*>(stage + Swz<D>::off(ln32, 4 * (cb0() + cb) + gr) + 8 * hh) = wv;
+        *reinterpret_cast<T4*>(stage + C::TILE + Swz<D>::off(ln32, 4 * (cb0() + cb) + gr) + 8 * hh) = wk;
       }
     wave_lds_sync();
     constexpr int CPR = 4 * C::NCBO;   // 16-byte chunks per row that this workgroup owns
@@ -423,7 +433,7 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
 #pragma unroll
     for (int i = 0; i < C::BT * CPR / 64; ++i) {
       const uint32_t c = 64 * i + lane;
-      const uint32_t r = c / CPR, x = 4 * cb0 + c % CPR;
+      const uint32_t r = c / CPR, x = 4 * cb0() + c % CPR;
       const u32x4 v = *reinterpret_cast<const u32x4*>(stage + Swz<D>::off(r, x));
       const u32x4 k = *reinterpret_cast<const u32x4*>(stage + C::TILE + Swz<D>::off(r, x));
       if (k0w + static_cast<int>(r) < sq.nk) {
