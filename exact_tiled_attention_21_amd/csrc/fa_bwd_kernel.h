@@ -321,6 +321,7 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
   // registers for its addresses to stay live that long, the caller issues it
   // before the step's first MFMA instead (kFetchAt < 0: no hook call here).
   static constexpr int kFetchAt = D <= 64 ? -1 : 4;
+  static constexpr int kFetchN = 2 * BwdDma<D, C::BQ>::C::NDMA + 1;   // DMA instructions of a fetch
   template <typename Hook>
   __device__ __forceinline__ void sdp(const char* qt, const char* ot, f32x16 (&s)[2], f32x16 (&dp)[2], Hook hook) const {
     s[0] = s[1] = dp[0] = dp[1] = f32x16{};
@@ -340,7 +341,7 @@ template <int D, bool BF16, bool BAND> struct DkdvWave {
     for (int m = 0; m < kSdMf; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (m + kPre < kSdMf) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (kFetchAt >= 0 && m >= kFetchAt && m < kFetchAt + 2 * BwdDma<D, C::BQ>::C::NDMA + 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      if (kFetchAt >= 0 && m >= kFetchAt && m < kFetchAt + kFetchN) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
     }
   }
 

@@ -19,12 +19,12 @@
 // of the whole GQA group (Hq/Hkv heads x Nq positions, at most 32 per row block)
 // share the part's K/V, which is therefore read from HBM once. The wave loads
 // each tile with fully coalesced, non-temporal 16-byte loads into registers
-// (one tile ahead, except at d = 192: about 16 MiB in flight chip-wide is enough for the HBM rate,
-// more only thins out the DRAM locality), stages it through its own swizzled
-// LDS tiles (K for the A operand, V for the transposing read), and writes one
-// normalised fp32 partial and its log-sum-exp per row; the combine kernel
-// merges the partials. No barriers between single waves: up to four share a CU,
-// one per SIMD.
+// (one tile ahead, except at d = 192: about 16 MiB in flight chip-wide is
+// enough for the HBM rate, more only thins out the DRAM locality), stages it
+// through its own swizzled LDS tiles (K for the A operand, V for the
+// transposing read), and writes one normalised fp32 partial and its
+// log-sum-exp per row; the combine kernel merges the partials. No barriers
+// between single waves: up to four share a CU, one per SIMD.
 //
 // Paged cache ("flash-attention-v100" README, flash_attn_with_kvcache: a block
 // table maps each sequence's logical key blocks to pages of a shared pool, and
