@@ -108,3 +108,16 @@ def test_decode_matches_forward():
     cmp.check_o(to_np(o1), ref[0], "bf16", "decode")
     cmp.check_o(to_np(o2), ref[0], "bf16", "fwd")
     assert float(np.abs(to_np(l1) - to_np(l2)).max()) <= 2e-3
+
+
+@pytest.mark.parametrize("d", [192, 256])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_large_head_dims_row_blocks(d, causal, dtype):
+    """The head dims whose split kernel loads each tile without running ahead
+    (192) or shares it between two waves that own half of O's columns each
+    (256): two 32-row blocks per KV head (group 8 x Nq 8), an odd batch, a
+    ragged cache, the causal mask and a negative scale."""
+    wid = 1200 + d + 2 * causal + (dtype == "bf16")
+    run(wid, 3, 8, 1000, 16, 2, d, dtype, 7, causal=causal)
+    run(wid + 10, 3, 8, 1000, 16, 2, d, dtype, 7, causal=causal, scale=-1.0 / math.sqrt(d))
