@@ -372,6 +372,80 @@ def sweep(args, torch, dev):
     return rows
 
 
+def smi_sample():
+    """Socket power (W) and the mean graphics clock (MHz) over the XCDs, from one
+    `amd-smi metric -p -c` reading; None where the tool is missing or says nothing."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                           timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    p = re.findall(r'"socket_power": \{\s*"value": ([0-9.]+)', r.stdout)
+    c = [float(x) for x in re.findall(r'"gfx_[0-7]": \{\s*"clk": \{\s*"value": ([0-9.]+)', r.stdout)]
+    if not p or not c:
+        return None
+    return float(p[0]), sum(c) / len(c)
+
+
+def power_probe(seconds, torch, attention):
+    """The [16,4096,32,128] f16 forward run back to back for `seconds` per input
+    set while another thread samples board power and clock: once with Gaussian
+    Q (the workload) and once with every Q element 1.0 (same instructions, same
+    K and V). The difference shows how far the matrix cores' switching, not the
+    instruction stream, sets the clock under the power limit."""
+    import threading
+    import synthetic
+    w = synthetic.WORKLOADS["long_f16_4096_full"]
+    out = {"workload": f"[{w.B},{w.Nq},{w.Hq},{w.d}] f16, no mask", "seconds": seconds}
+    for name in ("gaussian_q", "constant_q"):
+        q, k, v = device_inputs(w, torch, torch.device("cuda:0"))
+        if name == "constant_q":
+            q = torch.ones_like(q)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=q.device)
+        fn = lambda i=0: attention(q, k, v, causal=False, scale=w.scale, out=o, lse=lse)
+        prewarm(fn, 1.0, torch)
+        samples, done = [], threading.Event()
+
+        def sampler():
+            while not done.is_set():
+                x = smi_sample()
+                if x is not None:
+                    samples.append(x)
+                done.wait(0.5)
+        th = threading.Thread(target=sampler)
+        th.start()
+        t = timed_for(fn, seconds, torch)
+        done.set()
+        th.join()
+        row = {"tflops": round(w.flops() / (t * 1e-3) / 1e12, 1)}
+        if samples:
+            row["socket_power_w"] = round(statistics.mean(x[0] for x in samples), 1)
+            row["gfx_clock_mhz"] = round(statistics.mean(x[1] for x in samples), 1)
+            row["samples"] = len(samples)
+        out[name] = row
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    return out
+
+
+def timed_for(fn, seconds, torch):
+    """Mean ms per call of fn over at least `seconds` of back-to-back calls."""
+    n, t0 = 0, time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fn()
+        n += 20
+        torch.cuda.synchronize()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -393,6 +467,9 @@ def main():
                          "would pass 2^32)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (calibrates HBM byte counters)")
+    ap.add_argument("--power-probe", type=float, default=0.0, metavar="SECONDS",
+                    help="also run the N=4096 forward for SECONDS with Gaussian and with constant Q "
+                         "while sampling board power and clock (amd-smi)")
     ap.add_argument("--gemm-probe", type=int, default=0, metavar="N",
                     help="also time torch's fp16 N x N x N matmul (the library GEMM: the MFMA rate "
                          "and clock a tuned dense kernel sustains on this GPU)")
@@ -426,6 +503,9 @@ def main():
         torch.cuda.synchronize()
         result["copy_probe_bytes"] = 2 * src.numel()   # read + write
         del src, dst
+    if args.power_probe > 0:
+        result["power_probe"] = power_probe(args.power_probe, torch, attention)
+        progress(f"power probe: {result['power_probe']}")
     if args.gemm_probe:
         n = args.gemm_probe
         ga = torch.randn(n, n, device=dev, dtype=torch.float16)
