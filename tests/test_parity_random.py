@@ -1,0 +1,123 @@
+"""GPU parity against the fp64 oracle on seeded random configurations.
+
+The other parity files pick their shapes by hand (tile edges, ragged tails,
+every head dim, fully masked rows). This one draws the shape, head grouping,
+head dim, dtype, mask, scale and, for decode, the split count and paging from
+a fixed seed, so that combinations nobody listed are covered too. Sizes stay
+small enough for the oracle to finish in well under a second per case.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import test_parity_bwd as bwd
+import test_parity_decode as dec
+import test_parity_decode_paged as paged
+import test_parity_fwd as fwd
+import test_parity_fwd_window as win
+
+pytestmark = pytest.mark.gpu
+
+HEAD_DIMS = (32, 64, 96, 128, 192, 256)
+_rng = np.random.default_rng(20261203)
+
+
+def _heads():
+    hkv = int(_rng.choice([1, 2, 4]))
+    return hkv * int(_rng.choice([1, 2, 3, 4])), hkv
+
+
+def _scale(d):
+    # the default most of the time; otherwise a random magnitude and sign
+    if _rng.random() < 0.6:
+        return None
+    return float(_rng.choice([-1.0, 1.0]) * _rng.uniform(0.3, 2.0) / math.sqrt(d))
+
+
+def _mask(nq, nk):
+    r = _rng.random()
+    if r < 0.4:
+        return False, (-1, -1)
+    if r < 0.7:
+        return True, (-1, -1)
+    wl = int(_rng.choice([-1, int(_rng.integers(0, nk + 1))]))
+    wr = int(_rng.choice([-1, int(_rng.integers(0, nk + 1))]))
+    return False, (wl, wr)
+
+
+def _fwd_cases(n):
+    out = []
+    for i in range(n):
+        hq, hkv = _heads()
+        nq, nk = int(_rng.integers(1, 400)), int(_rng.integers(1, 400))
+        d = int(_rng.choice(HEAD_DIMS))
+        causal, window = _mask(nq, nk)
+        out.append((6000 + i, int(_rng.integers(1, 4)), nq, nk, hq, hkv, d, str(_rng.choice(["f16", "bf16"])),
+                    causal, window, _scale(d)))
+    return out
+
+
+def _bwd_cases(n):
+    out = []
+    for i in range(n):
+        hq, hkv = _heads()
+        nq, nk = int(_rng.integers(1, 300)), int(_rng.integers(1, 300))
+        d = int(_rng.choice(HEAD_DIMS))
+        causal, window = _mask(nq, nk)
+        out.append((6100 + i, int(_rng.integers(1, 3)), nq, nk, hq, hkv, d, str(_rng.choice(["f16", "bf16"])),
+                    causal, window, _scale(d)))
+    return out
+
+
+def _dec_cases(n):
+    out = []
+    for i in range(n):
+        hq, hkv = _heads()
+        d = int(_rng.choice(HEAD_DIMS))
+        nq = int(_rng.integers(1, 9))
+        page = int(_rng.choice([0, 32, 64, 256]))          # 0: contiguous cache
+        out.append((6200 + i, int(_rng.integers(1, 6)), nq, int(_rng.integers(1, 3000)), hq, hkv, d,
+                    str(_rng.choice(["f16", "bf16"])), int(_rng.integers(1, 65)), bool(_rng.random() < 0.3),
+                    page, _scale(d)))
+    return out
+
+
+FWD = _fwd_cases(80)
+BWD = _bwd_cases(48)
+DEC = _dec_cases(48)
+
+
+def _id(c):
+    return "-".join(str(x) for x in c[1:])
+
+
+@pytest.mark.parametrize("case", FWD, ids=_id)
+def test_forward(case):
+    wid, B, nq, nk, hq, hkv, d, dtype, causal, window, scale = case
+    if window == (-1, -1):
+        fwd.run_full(wid, B, nq, nk, hq, hkv, d, dtype, causal, scale=scale)
+    else:
+        win.run(wid, B, nq, nk, hq, hkv, d, dtype, window)
+
+
+@pytest.mark.parametrize("case", BWD, ids=_id)
+def test_backward(case):
+    wid, B, nq, nk, hq, hkv, d, dtype, causal, window, scale = case
+    bwd.run_full(wid, B, nq, nk, hq, hkv, d, dtype, causal, scale=scale, window=window)
+
+
+@pytest.mark.parametrize("case", DEC, ids=_id)
+def test_decode(case):
+    wid, B, nq, nk, hq, hkv, d, dtype, splits, causal, page, scale = case
+    if page == 0:
+        dec.run(wid, B, nq, nk, hq, hkv, d, dtype, splits, causal=causal, scale=scale)
+    else:
+        max_pages = (nk + page - 1) // page
+        lens = [int(x) for x in _lens(wid, B, max_pages * page)]
+        paged.run(wid, B, nq, hq, hkv, d, dtype, page, max_pages, lens, splits=splits, causal=causal, scale=scale)
+
+
+def _lens(wid, B, cap):
+    r = np.random.default_rng(wid)
+    return r.integers(0, cap + 1, size=B)
