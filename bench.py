@@ -7,7 +7,9 @@ also carries the split-KV decode step at B=8, Nq=1, Nk=8192, Hq=32, Hkv=8,
 d=128 bf16 with 16 splits, the forward at N=4096 (the 50%-of-peak target
 shape), a packed variable-length batch, the backward pass, and a sweep over the
 pages' other workloads (long sequences causal and not, the sharpened bf16
-repeat, the GQA head-dim sweep, decode with Nq=8; inputs drawn on the device).
+repeat, the GQA head-dim sweep, decode with Nq=8; inputs drawn on the device),
+and a power probe: board power and clock while the N=4096 forward runs with
+Gaussian and with constant Q.
 
 Timing: the headline times exactly --steps steps between two HIP events (its
 mean is `ms_per_step`); every other workload runs at least 50 steps and at least
@@ -467,9 +469,10 @@ def main():
                          "would pass 2^32)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (calibrates HBM byte counters)")
-    ap.add_argument("--power-probe", type=float, default=0.0, metavar="SECONDS",
-                    help="also run the N=4096 forward for SECONDS with Gaussian and with constant Q "
-                         "while sampling board power and clock (amd-smi)")
+    ap.add_argument("--power-probe", type=float, default=None, metavar="SECONDS",
+                    help="run the N=4096 forward for SECONDS with Gaussian and with constant Q "
+                         "while sampling board power and clock (amd-smi); 0 skips it (default: "
+                         "3 s in the full run, none with --only)")
     ap.add_argument("--gemm-probe", type=int, default=0, metavar="N",
                     help="also time torch's fp16 N x N x N matmul (the library GEMM: the MFMA rate "
                          "and clock a tuned dense kernel sustains on this GPU)")
@@ -503,9 +506,6 @@ def main():
         torch.cuda.synchronize()
         result["copy_probe_bytes"] = 2 * src.numel()   # read + write
         del src, dst
-    if args.power_probe > 0:
-        result["power_probe"] = power_probe(args.power_probe, torch, attention)
-        progress(f"power probe: {result['power_probe']}")
     if args.gemm_probe:
         n = args.gemm_probe
         ga = torch.randn(n, n, device=dev, dtype=torch.float16)
@@ -675,6 +675,11 @@ def main():
             progress(f"{wb.name}: {tb:.1f} TFLOP/s (pages' convention)")
             del q, k, v, do, o, lse, ws, dq, dk, dv
             torch.cuda.empty_cache()
+
+    probe_s = args.power_probe if args.power_probe is not None else (3.0 if args.only == "all" else 0.0)
+    if probe_s > 0:
+        result["power_probe"] = power_probe(probe_s, torch, attention)
+        progress(f"power probe: {result['power_probe']}")
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w)
