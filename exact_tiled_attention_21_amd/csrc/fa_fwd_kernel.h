@@ -20,7 +20,9 @@
 // tile's loads have a whole step to land. The kernel is held to 256 registers
 // or fewer (a few spilled at d = 256), so two workgroups (four at d = 32,
 // three at d = 64, 96 and 128) share a CU and each SIMD can interleave one
-// wave's exponentials with another wave's matrix products.
+// wave's exponentials with another wave's matrix products. Long fp16
+// sequences at d = 128 without a band use one wide workgroup per CU instead:
+// eight waves, 256 rows, two waves per SIMD (see FwdCfg).
 //
 // The reference max m used in P = exp2(s * scale * log2(e) - m) need not be
 // the running max: O and the row sum share it, so the result is the same for
@@ -36,7 +38,7 @@
 
 namespace fa {
 
-template <int D, bool BAND> struct FwdCfg {
+template <int D, bool BAND, bool WIDE = false> struct FwdCfg {
   // four waves, one per SIMD, and two or more workgroups per CU (several waves
   // per SIMD, each workgroup with its own barrier): a second (third, fourth) wave
   // overlaps one wave's softmax with another's products. Registers allow four
@@ -45,9 +47,14 @@ template <int D, bool BAND> struct FwdCfg {
   // d = 96 and 128 take 32-key tiles, which free the registers (and LDS) for a
   // third wave (with a band only without the per-wave skip of masked tiles,
   // which would make it spill).
-  static constexpr bool kNarrow = D == 96 || D == 128;
+  // WIDE (d = 128 fp16 without a band, long sequences): one workgroup of eight
+  // waves per CU, two per SIMD, 256 rows sharing each 64-key K/V tile, so each
+  // K/V byte crosses from L2 into LDS half as often per query row as with
+  // three 128-row workgroups.
+  static_assert(!WIDE || (D == 128 && !BAND), "the wide shape is d = 128 without a band");
+  static constexpr bool kNarrow = (D == 96 || D == 128) && !WIDE;
   static constexpr int WPE = (D <= 32) ? 4 : (D <= 64 || kNarrow) ? 3 : 2;
-  static constexpr int NW = 4;                       // waves per workgroup
+  static constexpr int NW = WIDE ? 8 : 4;            // waves per workgroup
   static constexpr int THREADS = NW * 64;
   static constexpr int BR = 32 * NW;                 // query rows per workgroup
   static constexpr int BC = (D <= 128 && !kNarrow) ? 64 : 32;    // keys per LDS tile
@@ -59,7 +66,7 @@ template <int D, bool BAND> struct FwdCfg {
   static constexpr int NPIECE = TILE_BYTES / 1024;           // 1 KB DMA pieces per tile
   static constexpr int NDMA = (NPIECE + NW - 1) / NW;        // pieces per wave (the last may idle)
   static constexpr bool EVEN = NPIECE % NW == 0;
-  static_assert(BR == fwd_rows(D), "rows per workgroup");
+  static_assert(BR == fwd_rows(D, WIDE), "rows per workgroup");
   static_assert(TILE_BYTES % 1024 == 0, "tile must split into whole DMA pieces");
 };
 
@@ -76,15 +83,15 @@ struct FwdSeq {
 
 // LDS of one workgroup: two stages each for K and V, as separate objects so the
 // compiler knows a DMA into one stage never feeds a read of the other.
-template <int D, bool BAND> struct FwdLds {
-  static constexpr int TB = FwdCfg<D, BAND>::TILE_BYTES;
+template <int D, bool BAND, bool WIDE = false> struct FwdLds {
+  static constexpr int TB = FwdCfg<D, BAND, WIDE>::TILE_BYTES;
   char* k[2];
   char* v[2];
 };
 
 // Per-wave state and the steps of the tile loop (device code only).
-template <int D, bool BF16, bool BAND> struct FwdWave {
-  using C = FwdCfg<D, BAND>;
+template <int D, bool BF16, bool BAND, bool WIDE = false> struct FwdWave {
+  using C = FwdCfg<D, BAND, WIDE>;
   using E = Elem<BF16>;
   using T = typename E::T;
   using V8 = typename E::V8;
@@ -380,7 +387,7 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
   // diagonal) or has no visible key; the other steps are straight-line code so
   // the O accumulators keep their registers across the loop.
   template <int ST, bool TAIL>
-  __device__ __forceinline__ void step(int j, const FwdLds<D, BAND>& lds) {
+  __device__ __forceinline__ void step(int j, const FwdLds<D, BAND, WIDE>& lds) {
     if (!kPreOfs) asm volatile("" : "+v"(kxo), "+v"(vx0), "+v"(vx1));
     if (j + 1 < jhi) {
       dma(kg, j + 1, lds.k[ST ^ 1]);
@@ -425,7 +432,7 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
   // directly writes 16 scattered bytes per row and instruction; instead the
   // wave's 32 x D tile of O goes through its own slice of the (now idle) K/V
   // LDS stages, and each 16-byte store instruction then writes whole rows.
-  __device__ __forceinline__ void finish(int hq, const FwdLds<D, BAND>& lds) {
+  __device__ __forceinline__ void finish(int hq, const FwdLds<D, BAND, WIDE>& lds) {
     const float l = halves_sum(l_part);
     const float l_lse = BF16 ? halves_sum(l_exact) : l;
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -464,10 +471,10 @@ template <int D, bool BF16, bool BAND> struct FwdWave {
   }
 };
 
-template <int D, bool BF16, bool BAND>
-__global__ __launch_bounds__((FwdCfg<D, BAND>::THREADS))
-__attribute__((amdgpu_waves_per_eu((FwdCfg<D, BAND>::WPE), (FwdCfg<D, BAND>::WPE)))) void fa_fwd_kernel(const FwdArgs a) {
-  using C = FwdCfg<D, BAND>;
+template <int D, bool BF16, bool BAND, bool WIDE = false>
+__global__ __launch_bounds__((FwdCfg<D, BAND, WIDE>::THREADS))
+__attribute__((amdgpu_waves_per_eu((FwdCfg<D, BAND, WIDE>::WPE), (FwdCfg<D, BAND, WIDE>::WPE)))) void fa_fwd_kernel(const FwdArgs a) {
+  using C = FwdCfg<D, BAND, WIDE>;
   __shared__ __attribute__((aligned(1024))) char k_lds0[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char k_lds1[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v_lds0[C::TILE_BYTES];
@@ -504,8 +511,8 @@ __attribute__((amdgpu_waves_per_eu((FwdCfg<D, BAND>::WPE), (FwdCfg<D, BAND>::WPE
                 (static_cast<size_t>(b) * a.Hq + hq) * a.Nq};
   }
 
-  FwdWave<D, BF16, BAND> w(a, sq, hq, g, qt);
-  const FwdLds<D, BAND> lds{{k_lds0, k_lds1}, {v_lds0, v_lds1}};
+  FwdWave<D, BF16, BAND, WIDE> w(a, sq, hq, g, qt);
+  const FwdLds<D, BAND, WIDE> lds{{k_lds0, k_lds1}, {v_lds0, v_lds1}};
   // tile j lives in stage (j - jlo) & 1; the first tile's DMA goes out before
   // the Q loads, so the prologue waits for one memory latency, not two
   if (w.jhi > w.jlo) {
@@ -555,6 +562,12 @@ hipError_t launch_fwd_d(const FwdArgs& a, bool bf16, bool band, hipStream_t stre
   const dim3 grid(static_cast<unsigned>(a.n_qtiles) * a.Hq * a.B);
   const dim3 block(C::THREADS);
   (void)hipGetLastError();   // start from a clean error state
+  if constexpr (D == 128) {
+    if (a.wide && !bf16 && !band) {   // n_qtiles then counts 256-row tiles
+      fa_fwd_kernel<D, false, false, true><<<grid, dim3(FwdCfg<D, false, true>::THREADS), 0, stream>>>(a);
+      return hipGetLastError();
+    }
+  }
   if (bf16) {
     if (band) fa_fwd_kernel<D, true, true><<<grid, block, 0, stream>>>(a);
     else fa_fwd_kernel<D, true, false><<<grid, block, 0, stream>>>(a);

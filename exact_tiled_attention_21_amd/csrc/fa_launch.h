@@ -27,6 +27,7 @@ struct FwdArgs {
   const int* cu_k;
   int total_q, total_k;
   int hb;          // heads per block of the heaviest-first order used with a band
+  int wide;        // d = 128 fp16 without a band: eight-wave workgroups of 256 rows
 };
 
 struct DecodeArgs {
@@ -90,7 +91,7 @@ inline int order_block_heads(long long nheads, long long bytes_per_head) {
 }
 
 // Rows of queries one forward workgroup covers (32 per wave).
-constexpr int fwd_rows(int) { return 128; }
+constexpr int fwd_rows(int, bool wide = false) { return wide ? 256 : 128; }
 
 // band: apply the (wl, wr) band (causal or a sliding window)
 hipError_t launch_fwd(const FwdArgs& a, int d, bool bf16, bool band, hipStream_t stream);

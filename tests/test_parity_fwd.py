@@ -186,3 +186,25 @@ def test_long_sequence_sampled(name):
 @pytest.mark.parametrize("name", GQA)
 def test_gqa_head_dim_sweep_sampled(name):
     run_sampled(synthetic.WORKLOADS[name], 13)
+
+
+@pytest.mark.parametrize("case", [(1, 3100, 700, 4, 2, None), (1, 3072, 3073, 2, 1, -0.05), (2, 4097, 300, 2, 2, None)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_wide_workgroups(case):
+    """fp16, d = 128, no mask, 3072 query rows or more: the eight-wave, 256-row
+    workgroup shape (64-key tiles). Whole tensors with a partial last row tile,
+    ragged key counts, grouped heads and a negative scale."""
+    B, nq, nk, hq, hkv, scale = case
+    run_full(7000 + nq % 97 + nk % 89, B, nq, nk, hq, hkv, 128, "f16", False, scale=scale)
+
+
+def test_wide_workgroups_rebase():
+    """Rising scores (as in test_reference_moves_in_unmasked_tiles) in the wide shape."""
+    B, N, H, d = 1, 3072, 2, 128
+    qb = synthetic.normal_bits(92, 0, (B, N, H, d), "f16")
+    kb = ramp_bits(92, 1, (B, N, H, d), "f16", 0.2, 4.0)
+    vb = synthetic.normal_bits(92, 2, (B, N, H, d), "f16")
+    o, lse = attention(to_dev(qb, "f16"), to_dev(kb, "f16"), to_dev(vb, "f16"), scale=0.5)
+    o_ref, lse_ref = oracle.attention_bits(qb, kb, vb, "f16", scale=0.5)
+    cmp.check_o(to_np(o), o_ref, "f16", "wide rising scores")
+    cmp.check_lse(to_np(lse), lse_ref, "wide rising scores")
