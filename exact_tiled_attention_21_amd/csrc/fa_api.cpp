@@ -163,13 +163,16 @@ fa_status fwd_common(fa::FwdArgs& a, int d, int wl, int wr, int causal, float sc
   a.negate_q = scale < 0.f;
   a.wl = wl;
   a.wr = causal ? 0 : wr;
+  const int64_t blocks = int64_t((a.Nq + fa::fwd_rows(d) - 1) / fa::fwd_rows(d)) * a.Hq * a.B;
+  if (blocks > kMaxGroupsX) return FA_ERR_SHAPE;
   // long fp16 sequences at d = 128 without a band take the eight-wave shape:
   // at 3072 rows and more it measured 3-4% faster, shorter ones and bf16 (whose
   // extra row sum wants the third wave per SIMD) gain nothing from it
   a.wide = d == 128 && dtype == FA_F16 && a.wl < 0 && a.wr < 0 && a.cu_q == nullptr && a.Nq >= 3072;
+  // its workgroups have 512 threads: keep the dispatch within 2^32 - 1 of them
+  if (a.wide && int64_t((a.Nq + fa::fwd_rows(d, true) - 1) / fa::fwd_rows(d, true)) * a.Hq * a.B > kMaxGroupsX / 2)
+    a.wide = 0;
   a.n_qtiles = (a.Nq + fa::fwd_rows(d, a.wide) - 1) / fa::fwd_rows(d, a.wide);
-  const int64_t blocks = int64_t(a.n_qtiles) * a.Hq * a.B;
-  if (blocks > kMaxGroupsX) return FA_ERR_SHAPE;
   // K and V bytes each query head reads (a group shares them)
   const int64_t kv_rows = a.cu_k ? int64_t(a.total_k) / a.B : a.Nk;
   a.hb = fa::order_block_heads(int64_t(a.Hq) * a.B, kv_rows * d * 4 / a.group);

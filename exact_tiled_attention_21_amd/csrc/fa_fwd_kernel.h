@@ -93,6 +93,7 @@ template <int D, bool BAND, bool WIDE = false> struct FwdLds {
 template <int D, bool BF16, bool BAND, bool WIDE = false> struct FwdWave {
   using C = FwdCfg<D, BAND, WIDE>;
   using E = Elem<BF16>;
+  static constexpr bool kBand = BAND;
   using T = typename E::T;
   using V8 = typename E::V8;
   typedef V8 PF[C::NT];
@@ -134,17 +135,25 @@ template <int D, bool BF16, bool BAND, bool WIDE = false> struct FwdWave {
     return (BAND && a.wr >= 0) ? min(sq.nk, i + diag + a.wr + 1) : sq.nk;
   }
 
-  __device__ __forceinline__ FwdWave(const FwdArgs& args, const FwdSeq& seq, int hq, int g, int qt)
+  __device__ __forceinline__ FwdWave(const FwdArgs& args, const FwdSeq& seq, int g, int qt)
       : a(args), sq(seq) {
     const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
     hh = lane >> 5;
     ln32 = lane & 31;
+    sl2 = a.sl2;
+    rowbytes = static_cast<uint32_t>(a.Hkv) * D * 2;
+    offsets();
+    begin(g, qt);
+  }
+
+  // The state of one query tile (rows of tile qt of sequence sq, KV head g):
+  // key extents, tile ranges, K/V sources, and cleared accumulators.
+  __device__ __forceinline__ void begin(int g, int qt) {
     q0w = qt * C::BR + wave * 32;
     qrow = q0w + ln32;
     diag = sq.nk - sq.nq;
-    sl2 = a.sl2;
 
     // Key extents. Row i sees keys j with i + diag - wl <= j <= i + diag + wr
     // (the band of a sliding window; causal is wl = none, wr = 0), clipped to
@@ -170,15 +179,27 @@ template <int D, bool BF16, bool BAND, bool WIDE = false> struct FwdWave {
     if (q0 + C::BR > sq.nq) jub = jua;   // a wave of this workgroup has no rows
     if (jub < jua) jub = jua;
 
-    // HBM -> LDS by DMA through buffer resources (rows >= Nk read as 0). DMA piece
-    // i of this wave fills LDS bytes [(i * NW + wave) * 1024, +1024): lane l writes
-    // 16 bytes at +16 l, i.e. physical chunk pch of row r, so it fetches logical
-    // chunk pch ^ swz(r) of that row.
-    rowbytes = static_cast<uint32_t>(a.Hkv) * D * 2;
-    const size_t head_off = (sq.k_row0 * a.Hkv + g) * D * 2;
-    kg = reinterpret_cast<const char*>(a.k) + head_off;
-    vg = reinterpret_cast<const char*>(a.v) + head_off;
+    // HBM -> LDS by DMA through buffer resources (rows >= Nk read as 0)
+    kg = kv_base(a.k, g);
+    vg = kv_base(a.v, g);
     valid = static_cast<int64_t>(sq.nk - 1) * rowbytes + D * 2;
+
+#pragma unroll
+    for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] = f32x16{};
+    m_run = kNegInf;
+    l_part = 0.f;
+    l_exact = 0.f;
+  }
+
+  // first K (or V) row of KV head g of the sequence
+  __device__ __forceinline__ const char* kv_base(const void* base, int g) const {
+    return reinterpret_cast<const char*>(base) + (sq.k_row0 * a.Hkv + g) * D * 2;
+  }
+
+  // Offsets that depend on the lane only. DMA piece i of this wave fills LDS bytes
+  // [(i * NW + wave) * 1024, +1024): lane l writes 16 bytes at +16 l, i.e.
+  // physical chunk pch of row r, so it fetches logical chunk pch ^ swz(r) of that row.
+  __device__ __forceinline__ void offsets() {
 #pragma unroll
     for (int i = 0; i < C::NDMA; ++i) {
       const uint32_t p = (i * C::NW + wave) * 1024 + lane * 16;
@@ -206,24 +227,23 @@ template <int D, bool BF16, bool BAND, bool WIDE = false> struct FwdWave {
       vlo[cb] = (vx0 ^ (64u * cb)) + vb0;
       vhi[cb] = (vx1 ^ (64u * cb)) + vb1;
     }
-
-#pragma unroll
-    for (int cb = 0; cb < C::NCB; ++cb) oacc[cb] = f32x16{};
-    m_run = kNegInf;
-    l_part = 0.f;
-    l_exact = 0.f;
   }
 
   // Q fragment (B operand): Q[qrow][16s + 8hh .. +7], sign-flipped for a negative
   // scale. All loads are issued before the flip, which waits for them once.
   __device__ __forceinline__ void load_q(int hq) {
-    const T* qp = reinterpret_cast<const T*>(a.q) +
-                  ((sq.q_row0 + qrow) * a.Hq + hq) * D + 8 * hh;
+    fetch_q(qf, sq, qrow, hq);
+    flip_q(qf);
+  }
+  __device__ __forceinline__ void fetch_q(V8 (&dst)[C::NS], const FwdSeq& s_, int row, int hq) const {
+    const T* qp = reinterpret_cast<const T*>(a.q) + ((s_.q_row0 + row) * a.Hq + hq) * D + 8 * hh;
 #pragma unroll
-    for (int s = 0; s < C::NS; ++s) qf[s] = qrow < sq.nq ? *reinterpret_cast<const V8*>(qp + 16 * s) : V8{};
+    for (int s = 0; s < C::NS; ++s) dst[s] = row < s_.nq ? *reinterpret_cast<const V8*>(qp + 16 * s) : V8{};
+  }
+  __device__ __forceinline__ void flip_q(V8 (&f)[C::NS]) const {
     if (a.negate_q) {
 #pragma unroll
-      for (int s = 0; s < C::NS; ++s) qf[s] = -qf[s];
+      for (int s = 0; s < C::NS; ++s) f[s] = -f[s];
     }
   }
 
@@ -433,15 +453,17 @@ template <int D, bool BF16, bool BAND, bool WIDE = false> struct FwdWave {
   // wave's 32 x D tile of O goes through its own slice of the (now idle) K/V
   // LDS stages, and each 16-byte store instruction then writes whole rows.
   __device__ __forceinline__ void finish(int hq, const FwdLds<D, BAND, WIDE>& lds) {
+    constexpr int WPS = C::BC / 32;                // waves per LDS stage
+    const int st = wave / WPS;
+    finish_via(hq, (st == 0 ? lds.k[0] : st == 1 ? lds.k[1] : st == 2 ? lds.v[0] : lds.v[1]) +
+                       (wave % WPS) * (32 * D * 2));
+  }
+  // the same through the wave's own [32][D] slice `ot` of some LDS buffer
+  __device__ __forceinline__ void finish_via(int hq, char* const ot) {
     const float l = halves_sum(l_part);
     const float l_lse = BF16 ? halves_sum(l_exact) : l;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     // this wave's tile: [32][D] of the element type, 16-byte chunks swizzled by row
-    constexpr int WPS = C::BC / 32;                // waves per LDS stage
-    constexpr uint32_t kRowB = D * 2;
-    const int st = wave / WPS;
-    char* const ot = (st == 0 ? lds.k[0] : st == 1 ? lds.k[1] : st == 2 ? lds.v[0] : lds.v[1]) +
-                     (wave % WPS) * (32 * kRowB);
     typedef T T4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int cb = 0; cb < C::NCB; ++cb)
@@ -470,6 +492,49 @@ template <int D, bool BF16, bool BAND, bool WIDE = false> struct FwdWave {
           l_lse > 0.f ? (m_run + __log2f(l_lse)) * kLn2 : kNegInf;
   }
 };
+
+// The tile loop of one query tile: masked tiles before the unmasked run (the
+// left edge of a band; all of them when there is no unmasked run), the unmasked
+// run two tiles per iteration with compile-time stages, then the masked tiles
+// after it (key tail, diagonal, right edge of a band). Tile j lives in stage
+// (j - jlo) & 1.
+template <class W, class L>
+__device__ __forceinline__ void fwd_tiles(W& w, const L& lds) {
+  int j = w.jlo;
+  // masked tiles before the unmasked run (the left edge of a band); all of
+  // them when there is no unmasked run. Without a band the unmasked run starts
+  // at the first tile, and the masked tiles after it are all there is otherwise.
+  if constexpr (W::kBand) {
+    const int head_end = w.jub > w.jua ? w.jua : w.jhi;
+    for (; j + 2 <= head_end; j += 2) {   // j - jlo is even here
+      w.template step<0, true>(j, lds);
+      w.template step<1, true>(j + 1, lds);
+    }
+    if (j < head_end) {
+      w.template step<0, true>(j, lds);
+      ++j;
+    }
+  }
+  // the unmasked run, two tiles per iteration with compile-time stages
+  if (j < w.jub && ((j - w.jlo) & 1)) {
+    w.template step<1, false>(j, lds);
+    ++j;
+  }
+  for (; j + 2 <= w.jub; j += 2) {
+    w.template step<0, false>(j, lds);
+    w.template step<1, false>(j + 1, lds);
+  }
+  // masked tiles after it (key tail, diagonal, right edge of a band)
+  if (j < w.jhi && ((j - w.jlo) & 1)) {
+    w.template step<1, true>(j, lds);
+    ++j;
+  }
+  for (; j + 2 <= w.jhi; j += 2) {
+    w.template step<0, true>(j, lds);
+    w.template step<1, true>(j + 1, lds);
+  }
+  if (j < w.jhi) w.template step<0, true>(j, lds);
+}
 
 template <int D, bool BF16, bool BAND, bool WIDE = false>
 __global__ __launch_bounds__((FwdCfg<D, BAND, WIDE>::THREADS))
@@ -511,7 +576,7 @@ __attribute__((amdgpu_waves_per_eu((FwdCfg<D, BAND, WIDE>::WPE), (FwdCfg<D, BAND
                 (static_cast<size_t>(b) * a.Hq + hq) * a.Nq};
   }
 
-  FwdWave<D, BF16, BAND, WIDE> w(a, sq, hq, g, qt);
+  FwdWave<D, BF16, BAND, WIDE> w(a, sq, g, qt);
   const FwdLds<D, BAND, WIDE> lds{{k_lds0, k_lds1}, {v_lds0, v_lds1}};
   // tile j lives in stage (j - jlo) & 1; the first tile's DMA goes out before
   // the Q loads, so the prologue waits for one memory latency, not two
@@ -521,37 +586,7 @@ __attribute__((amdgpu_waves_per_eu((FwdCfg<D, BAND, WIDE>::WPE), (FwdCfg<D, BAND
   }
   w.load_q(hq);
   __syncthreads();
-  int j = w.jlo;
-  // masked tiles before the unmasked run (the left edge of a band); all of
-  // them when there is no unmasked run
-  const int head_end = w.jub > w.jua ? w.jua : w.jhi;
-  for (; j + 2 <= head_end; j += 2) {   // j - jlo is even here
-    w.template step<0, true>(j, lds);
-    w.template step<1, true>(j + 1, lds);
-  }
-  if (j < head_end) {
-    w.template step<0, true>(j, lds);
-    ++j;
-  }
-  // the unmasked run, two tiles per iteration with compile-time stages
-  if (j < w.jub && ((j - w.jlo) & 1)) {
-    w.template step<1, false>(j, lds);
-    ++j;
-  }
-  for (; j + 2 <= w.jub; j += 2) {
-    w.template step<0, false>(j, lds);
-    w.template step<1, false>(j + 1, lds);
-  }
-  // masked tiles after it (key tail, diagonal, right edge of a band)
-  if (j < w.jhi && ((j - w.jlo) & 1)) {
-    w.template step<1, true>(j, lds);
-    ++j;
-  }
-  for (; j + 2 <= w.jhi; j += 2) {
-    w.template step<0, true>(j, lds);
-    w.template step<1, true>(j + 1, lds);
-  }
-  if (j < w.jhi) w.template step<0, true>(j, lds);
+  fwd_tiles(w, lds);
   w.finish(hq, lds);
 }
 
