@@ -188,12 +188,14 @@ def test_gqa_head_dim_sweep_sampled(name):
     run_sampled(synthetic.WORKLOADS[name], 13)
 
 
-@pytest.mark.parametrize("case", [(1, 3100, 700, 4, 2, None), (1, 3072, 3073, 2, 1, -0.05), (2, 4097, 300, 2, 2, None)],
+@pytest.mark.parametrize("case", [(1, 3100, 700, 4, 2, None), (1, 3072, 3073, 2, 1, -0.05), (2, 4097, 300, 2, 2, None),
+                                  (1, 3072, 17, 2, 2, None), (1, 3333, 64, 2, 1, None)],
                          ids=lambda c: "x".join(map(str, c)))
 def test_wide_workgroups(case):
     """fp16, d = 128, no mask, 3072 query rows or more: the eight-wave, 256-row
     workgroup shape (64-key tiles). Whole tensors with a partial last row tile,
-    ragged key counts, grouped heads and a negative scale."""
+    ragged key counts (also fewer keys than one tile, and exactly one tile),
+    grouped heads and a negative scale."""
     B, nq, nk, hq, hkv, scale = case
     run_full(7000 + nq % 97 + nk % 89, B, nq, nk, hq, hkv, 128, "f16", False, scale=scale)
 
