@@ -9,7 +9,7 @@ shape), a packed variable-length batch, the backward pass, and a sweep over the
 pages' other workloads (long sequences causal and not, the sharpened bf16
 repeat, the GQA head-dim sweep, decode with Nq=8; inputs drawn on the device),
 and a power probe: board power and clock while the N=4096 forward runs with
-Gaussian and with constant Q.
+Gaussian and with constant Q, and while the headline runs.
 
 Timing: the headline times exactly --steps steps between two HIP events (its
 mean is `ms_per_step`); every other workload runs at least 50 steps and at least
@@ -396,12 +396,14 @@ def power_probe(seconds, torch, attention):
     set while another thread samples board power and clock: once with Gaussian
     Q (the workload) and once with every Q element 1.0 (same instructions, same
     K and V). The difference shows how far the matrix cores' switching, not the
-    instruction stream, sets the clock under the power limit."""
+    instruction stream, sets the clock under the power limit. Then the headline
+    workload [16,1024,32,128] with its Gaussian inputs, the same way."""
     import threading
     import synthetic
-    w = synthetic.WORKLOADS["long_f16_4096_full"]
-    out = {"workload": f"[{w.B},{w.Nq},{w.Hq},{w.d}] f16, no mask", "seconds": seconds}
-    for name in ("gaussian_q", "constant_q"):
+    w4 = synthetic.WORKLOADS["long_f16_4096_full"]
+    wh = synthetic.WORKLOADS["headline_f16_1024"]
+    out = {"workload": f"[{w4.B},{w4.Nq},{w4.Hq},{w4.d}] f16, no mask", "seconds": seconds}
+    for name, w in (("gaussian_q", w4), ("constant_q", w4), ("headline_gaussian_q", wh)):
         q, k, v = device_inputs(w, torch, torch.device("cuda:0"))
         if name == "constant_q":
             q = torch.ones_like(q)
@@ -423,6 +425,8 @@ def power_probe(seconds, torch, attention):
         done.set()
         th.join()
         row = {"tflops": round(w.flops() / (t * 1e-3) / 1e12, 1)}
+        if w is not w4:
+            row["workload"] = f"[{w.B},{w.Nq},{w.Hq},{w.d}] f16, no mask"
         if samples:
             row["socket_power_w"] = round(statistics.mean(x[0] for x in samples), 1)
             row["gfx_clock_mhz"] = round(statistics.mean(x[1] for x in samples), 1)
