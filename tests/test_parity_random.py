@@ -2,9 +2,11 @@
 
 The other parity files pick their shapes by hand (tile edges, ragged tails,
 every head dim, fully masked rows). This one draws the shape, head grouping,
-head dim, dtype, mask, scale and, for decode, the split count and paging from
-a fixed seed, so that combinations nobody listed are covered too. Sizes stay
-small enough for the oracle to finish in well under a second per case.
+head dim, dtype, mask, scale, for decode the split count and paging, and for
+packed batches the number of sequences and their query and key lengths (empty
+ones included) from a fixed seed, so that combinations nobody listed are
+covered too. Sizes stay small enough for the oracle to finish in well under a
+second per case.
 """
 import math
 
@@ -12,9 +14,11 @@ import numpy as np
 import pytest
 
 import test_parity_bwd as bwd
+import test_parity_bwd_varlen as bvl
 import test_parity_decode as dec
 import test_parity_decode_paged as paged
 import test_parity_fwd as fwd
+import test_parity_fwd_varlen as fvl
 import test_parity_fwd_window as win
 
 pytestmark = pytest.mark.gpu
@@ -83,9 +87,28 @@ def _dec_cases(n):
     return out
 
 
+def _varlen_cases(n, base, maxlen):
+    out = []
+    for i in range(n):
+        hq, hkv = _heads()
+        nseq = int(_rng.integers(1, 7))
+        lq = [int(x) for x in _rng.integers(0, maxlen + 1, size=nseq)]
+        # self-attention lengths most of the time, otherwise independent key lengths
+        lk = list(lq) if _rng.random() < 0.5 else [int(x) for x in _rng.integers(0, maxlen + 1, size=nseq)]
+        if sum(lq) == 0:
+            lq[0] = 1
+        if sum(lk) == 0:
+            lk[0] = 1
+        out.append((base + i, tuple(lq), tuple(lk), hq, hkv, int(_rng.choice(HEAD_DIMS)),
+                    str(_rng.choice(["f16", "bf16"])), bool(_rng.random() < 0.5)))
+    return out
+
+
 FWD = _fwd_cases(80)
 BWD = _bwd_cases(48)
 DEC = _dec_cases(48)
+FVL = _varlen_cases(24, 6300, 300)
+BVL = _varlen_cases(16, 6400, 200)
 
 
 def _id(c):
@@ -121,3 +144,19 @@ def test_decode(case):
 def _lens(wid, B, cap):
     r = np.random.default_rng(wid)
     return r.integers(0, cap + 1, size=B)
+
+
+def _vid(c):
+    return f"{len(c[1])}seq-{c[3]}-{c[4]}-{c[5]}-{c[6]}-{'causal' if c[7] else 'full'}-{c[0]}"
+
+
+@pytest.mark.parametrize("case", FVL, ids=_vid)
+def test_forward_varlen(case):
+    wid, lq, lk, hq, hkv, d, dtype, causal = case
+    fvl.run(wid, lq, lk, hq, hkv, d, dtype, causal=causal)
+
+
+@pytest.mark.parametrize("case", BVL, ids=_vid)
+def test_backward_varlen(case):
+    wid, lq, lk, hq, hkv, d, dtype, causal = case
+    bvl.run(wid, lq, lk, hq, hkv, d, dtype, causal=causal)
