@@ -22,10 +22,12 @@ def qkv(wid, B, Nq, Nk, Hq, Hkv, d, dtype):
             to_dev(synthetic.normal_bits(wid, 2, (B, Nk, Hkv, d), dtype), dtype))
 
 
-@pytest.mark.parametrize("causal", [False, True])
-def test_forward_is_bitwise_deterministic(causal):
+@pytest.mark.parametrize("causal,nq", [(False, 1000), (True, 1000), (False, 3300)],
+                         ids=["full", "causal", "wide"])
+def test_forward_is_bitwise_deterministic(causal, nq):
+    # nq = 3300 (fp16, d = 128, no mask) runs the 256-row workgroup shape
     import torch
-    q, k, v = qkv(1000, 2, 1000, 1000, 8, 4, 128, "f16")
+    q, k, v = qkv(1000, 2, nq, 1000, 8, 4, 128, "f16")
     o1, l1 = attention(q, k, v, causal=causal)
     o2, l2 = attention(q, k, v, causal=causal)
     torch.cuda.synchronize()
@@ -51,13 +53,17 @@ def canary_view(n_elems, dtype, pad=4096):
     return buf, buf[pad:pad + n_elems], pad
 
 
-def test_forward_writes_every_output_and_nothing_else():
+@pytest.mark.parametrize("shape", [(2, 333, 200, 6, 3, 64, "bf16", True), (1, 3100, 130, 4, 2, 128, "f16", False)],
+                         ids=["causal-d64", "wide-d128"])
+def test_forward_writes_every_output_and_nothing_else(shape):
+    # the second shape (fp16, d = 128, no mask, 3100 rows) runs the 256-row workgroups
     import torch
-    B, Nq, Nk, Hq, Hkv, d = 2, 333, 200, 6, 3, 64
-    q, k, v = qkv(1002, B, Nq, Nk, Hq, Hkv, d, "bf16")
-    obuf, o, pad = canary_view(B * Nq * Hq * d, torch.bfloat16)
+    B, Nq, Nk, Hq, Hkv, d, dtype, causal = shape
+    q, k, v = qkv(1002, B, Nq, Nk, Hq, Hkv, d, dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    obuf, o, pad = canary_view(B * Nq * Hq * d, tdt)
     lbuf, lse, lpad = canary_view(B * Hq * Nq, torch.float32)
-    attention(q, k, v, causal=True, out=o.view(B, Nq, Hq, d), lse=lse.view(B, Hq, Nq))
+    attention(q, k, v, causal=causal, out=o.view(B, Nq, Hq, d), lse=lse.view(B, Hq, Nq))
     torch.cuda.synchronize()
     assert not torch.isnan(o.float()).any()
     assert not torch.isnan(lse).any()          # fully masked rows are -inf, never NaN
