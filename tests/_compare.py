@@ -1,22 +1,29 @@
 """Tolerance rules used by the GPU parity tests.
 
 Output O (fp16/bf16) against the fp64 oracle:
-  max over elements of (|O_gpu - O_ref| - ulp(O_ref)/2) <= 1e-2
-  mean over elements of |O_gpu - O_ref|                <= 1e-3
+  max over elements of  (|O_gpu - O_ref| - ulp(O_ref)/2)    <= 1e-2
+  mean over elements of max(0, |O_gpu - O_ref| - ulp(O_ref)/2) <= 1e-3
 The half-ulp allowance is the error of rounding the exact result to the output
 type; without it no bf16 output could meet 1e-2 where |O| >= 4 (bf16 spacing
-there is 2^-5). LSE (fp32): |LSE_gpu - LSE_ref| <= 1e-3 where finite, and both
--inf exactly where a row sees no key.
+there is 2^-5), nor the mean bound where |O| is near 1 (a sequence of two keys:
+the correctly rounded bf16 result alone is 9.1e-4 off on average). LSE (fp32):
+|LSE_gpu - LSE_ref| <= 1e-3 where finite, and both -inf exactly where a row
+sees no key.
 
 Gradients dQ, dK, dV (fp16/bf16) against the fp64 oracle, element by element:
-  |G_gpu - G_ref| - ulp(G_ref)/2 <= 2 u M
-with u the unit roundoff of the input type (2^-8 bf16, 2^-11 fp16) and M the
+  |G_gpu - G_ref| - ulp(G_ref)/2 <= 2 (u M + eta F)
+with u the unit roundoff of the input type (2^-8 bf16, 2^-11 fp16), M the
 sum of the magnitudes of the terms the element adds up (oracle
-backward_magnitudes). An implementation that rounds P and dS to the input type
-as MFMA operands, accumulates in fp32 and forms D from its rounded O has an
-error of at most about u M; a float32 emulation of that arithmetic reaches
-0.84 u M on the test shapes, and a dropped D term, a causal mask one key off
-or two swapped dO rows exceed the bound 3x to 10^5x.
+backward_magnitudes), eta half the type's smallest subnormal spacing (2^-25
+fp16, 2^-134 bf16) and F the sum of the magnitudes of the factors P and dS are
+multiplied by (oracle backward_operand_sums; callers that pass none get F = 0).
+An implementation that rounds P and dS to the input type as MFMA operands,
+accumulates in fp32 and forms D from its rounded O has an error of at most about
+u M + eta F: the rounding is relative (u) in the normal range and absolute (eta)
+below it, where a probability of a key that a single row barely sees can land
+(fp16 P near 6e-6: half an ulp is 0.5% of it). A float32 emulation of that
+arithmetic reaches 0.84 u M on the test shapes, and a dropped D term, a causal
+mask one key off or two swapped dO rows exceed the bound 3x to 10^5x.
 
 Secondary rule (the upstream test criterion, "flash-attention-v100" README,
 Tests: the output and the gradients have at most twice the error of a baseline
@@ -54,39 +61,49 @@ def check_o(o_gpu, o_ref, dtype, what=""):
     err = np.abs(o_gpu - o_ref)
     excess = err - 0.5 * ulp(o_ref, dtype)
     worst = float(excess.max()) if err.size else 0.0
-    mean = float(err.mean()) if err.size else 0.0
-    stats = dict(max_err=float(err.max()) if err.size else 0.0, max_excess=worst, mean_err=mean)
+    mean = float(np.maximum(excess, 0.0).mean()) if err.size else 0.0
+    stats = dict(max_err=float(err.max()) if err.size else 0.0, max_excess=worst,
+                 mean_err=float(err.mean()) if err.size else 0.0, mean_excess=mean)
     assert worst <= MAX_TOL, f"{what}: max |dO| - ulp/2 = {worst:.3g} > {MAX_TOL} {stats}"
-    assert mean <= MEAN_TOL, f"{what}: mean |dO| = {mean:.3g} > {MEAN_TOL} {stats}"
+    assert mean <= MEAN_TOL, f"{what}: mean (|dO| - ulp/2)+ = {mean:.3g} > {MEAN_TOL} {stats}"
     return stats
 
 
 UNIT_ROUNDOFF = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+SUBNORMAL_HALF = {"f16": 2.0 ** -25, "bf16": 2.0 ** -134}
 GRAD_BOUND = 2.0
 
 
-def grad_ratios(g_gpu, g_ref, mag, dtype):
-    """Per element: (|G - G_ref| - ulp(G_ref)/2) / (u M), 0 where within half an ulp."""
+def grad_bound(mag, dtype, floor=None):
+    """u M + eta F per element (F = 0 without `floor`)."""
+    b = UNIT_ROUNDOFF[dtype] * np.asarray(mag, np.float64)
+    if floor is not None:
+        b = b + SUBNORMAL_HALF[dtype] * np.asarray(floor, np.float64)
+    return b
+
+
+def grad_ratios(g_gpu, g_ref, mag, dtype, floor=None):
+    """Per element: (|G - G_ref| - ulp(G_ref)/2) / (u M + eta F), 0 where within half an ulp."""
     g_gpu = np.asarray(g_gpu, np.float64)
     g_ref = np.asarray(g_ref, np.float64)
     excess = np.abs(g_gpu - g_ref) - 0.5 * ulp(g_ref, dtype)
-    bound = UNIT_ROUNDOFF[dtype] * np.asarray(mag, np.float64)
+    bound = grad_bound(mag, dtype, floor)
     return np.where(excess > 0, excess / np.maximum(bound, 1e-300), 0.0)
 
 
-def check_grad(g_gpu, g_ref, mag, dtype, what=""):
+def check_grad(g_gpu, g_ref, mag, dtype, what="", floor=None):
     """Element-wise rounding-error bound on a gradient (rule above)."""
     g_gpu = np.asarray(g_gpu, np.float64)
     g_ref = np.asarray(g_ref, np.float64)
     assert g_gpu.shape == g_ref.shape, (g_gpu.shape, g_ref.shape)
     assert np.all(np.isfinite(g_gpu)), f"{what}: non-finite gradient"
-    bound = UNIT_ROUNDOFF[dtype] * np.asarray(mag, np.float64)
-    ratio = grad_ratios(g_gpu, g_ref, mag, dtype)
+    bound = grad_bound(mag, dtype, floor)
+    ratio = grad_ratios(g_gpu, g_ref, mag, dtype, floor)
     worst = float(ratio.max()) if ratio.size else 0.0
     if worst > GRAD_BOUND:
         i = np.unravel_index(int(ratio.argmax()), ratio.shape)
-        raise AssertionError(f"{what}: |dG| = {abs(g_gpu[i] - g_ref[i]):.3g} at {i} exceeds {GRAD_BOUND} u M "
-                             f"(u M = {bound[i]:.3g}, ref {g_ref[i]:.3g}, gpu {g_gpu[i]:.3g}); "
+        raise AssertionError(f"{what}: |dG| = {abs(g_gpu[i] - g_ref[i]):.3g} at {i} exceeds {GRAD_BOUND} (u M + eta F) "
+                             f"(u M + eta F = {bound[i]:.3g}, ref {g_ref[i]:.3g}, gpu {g_gpu[i]:.3g}); "
                              f"ratio {worst:.3g}")
     return worst
 
