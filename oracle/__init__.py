@@ -11,6 +11,9 @@ Contents
                      upstream dO), written out with numpy matrix products
   backward_magnitudes()  per gradient element, the sum of the magnitudes of
                      the terms it adds up (the scale of its rounding error)
+  backward_operand_sums()  per gradient element, the sum of the magnitudes of
+                     the factors P and dS are multiplied by (the scale of the
+                     error of rounding P and dS below the normal range)
   mask_matrix()      the visibility rule of visible() as a boolean matrix
   brute_force()      the same definition as plain Python loops with math.fsum,
                      for tiny shapes; it cross-checks the C routine
@@ -292,3 +295,33 @@ def backward_magnitudes(q, k, v, do, causal=False, scale=None, window=(-1, -1)):
             mk[b, :, g] += abs(scale) * (a_s.T @ np.abs(qh))
             mv[b, :, g] += p.T @ np.abs(doh)
     return mq, mk, mv
+
+
+def backward_operand_sums(q, k, do, causal=False, scale=None, window=(-1, -1)):
+    """fp64 sums (fq, fk, fv) of the factors that multiply P and dS in backward()'s
+    products, over the (row, key) pairs that see each other:
+      fv[j, c] = sum_i |dO_ic|,  fk[j, c] = |scale| sum_i |Q_ic|,  fq[i, c] = |scale| sum_j |K_jc|,
+    group-summed over the query heads of a key/value head like the gradients.
+    Rounding a probability or a dS value to a 16-bit type where it lies below the
+    type's normal range has an absolute error of up to half the subnormal spacing
+    rather than a relative one; these sums carry that error into each gradient
+    element (q and k as [B, N, H, d], do like q)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    do = np.asarray(do, np.float64)
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    group = Hq // Hkv
+    vis = mask_matrix(Nq, Nk, causal, window).astype(np.float64)
+    fq = np.zeros_like(q)
+    fk = np.zeros_like(k)
+    fv = np.zeros_like(k)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            fq[b, :, h] = abs(scale) * (vis @ np.abs(k[b, :, g]))
+            fk[b, :, g] += abs(scale) * (vis.T @ np.abs(q[b, :, h]))
+            fv[b, :, g] += vis.T @ np.abs(do[b, :, h])
+    return fq, fk, fv

@@ -1,7 +1,8 @@
-"""CPU pins of the gradient tolerance: oracle.backward_magnitudes against closed
-forms, and the element-wise rule of _compare.check_grad against mistakes planted
-in a copy of the oracle's gradient arithmetic (on the CPU) and against a plain
-float32 implementation of the kernels' arithmetic.
+"""CPU pins of the gradient tolerance: oracle.backward_magnitudes and
+oracle.backward_operand_sums against closed forms, and the element-wise rule of
+_compare.check_grad against mistakes planted in a copy of the oracle's gradient
+arithmetic (on the CPU), against a plain float32 implementation of the kernels'
+arithmetic, and on a subnormal fp16 probability worked by hand.
 
 backward_magnitudes sets the scale of every dQ, dK, dV tolerance, so it is pinned
 from both sides: exact values where the sums have a closed form (one visible key,
@@ -166,3 +167,69 @@ def test_rule_accepts_float32_arithmetic(dtype, causal):
     emu = cmp.emulate_backward(q, k, v, do, causal, sc, dtype)
     for g, r, m, n in zip(emu, ref, mag, ("dq", "dk", "dv")):
         assert cmp.check_grad(g, r, m, dtype, n) <= 1.0
+
+
+# ------------------------------------------------- the rounding below normal range
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_operand_sums_with_one_visible_key(causal):
+    """One key: every row that sees it multiplies its P (and dS) by dO (and Q, K) once:
+      fv[0, c] = sum_{h in group, i} |dO_ic|,  fk[0, c] = |scale| sum_{h in group, i} |Q_ic|,
+      fq[i, c] = |scale| |K_0c|,
+    over the rows that see the key (causal with Nq = 3 > Nk = 1: only row 2)."""
+    B, Nq, Nk, Hq, Hkv, d = 2, 3, 1, 4, 2, 5
+    q, k, do = rand(B, Nq, Hq, d), rand(B, Nk, Hkv, d), rand(B, Nq, Hq, d)
+    scale = -0.7
+    fq, fk, fv = oracle.backward_operand_sums(q, k, do, causal=causal, scale=scale)
+    group = Hq // Hkv
+    eq, ek, ev = np.zeros_like(q), np.zeros_like(k), np.zeros_like(k)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            for i in range(Nq):
+                if causal and i < Nq - 1:
+                    continue   # only the last row sees the key
+                for c in range(d):
+                    eq[b, i, h, c] = abs(scale) * abs(k[b, 0, g, c])
+                    ek[b, 0, g, c] += abs(scale) * abs(q[b, i, h, c])
+                    ev[b, 0, g, c] += abs(do[b, i, h, c])
+    np.testing.assert_allclose(fq, eq, rtol=1e-13, atol=1e-300)
+    np.testing.assert_allclose(fk, ek, rtol=1e-13, atol=1e-300)
+    np.testing.assert_allclose(fv, ev, rtol=1e-13, atol=1e-300)
+
+
+def test_operand_sums_count_each_visible_pair_once():
+    """Causal, Nq = Nk = 4, d = 1, every |Q| = |K| = |dO| = 1, scale 1: key j is
+    seen by rows j..3 and row i sees keys 0..i, so fv = fk = (4, 3, 2, 1) and
+    fq = (1, 2, 3, 4)."""
+    one = np.ones((1, 4, 1, 1))
+    fq, fk, fv = oracle.backward_operand_sums(one, -one, one, causal=True, scale=1.0)
+    np.testing.assert_array_equal(fv[0, :, 0, 0], [4, 3, 2, 1])
+    np.testing.assert_array_equal(fk[0, :, 0, 0], [4, 3, 2, 1])
+    np.testing.assert_array_equal(fq[0, :, 0, 0], [1, 2, 3, 4])
+
+
+def test_subnormal_probability_needs_the_absolute_term():
+    """One query, two keys, d = 1, scale 1, fp16: q = 1, k = (0, s), v = (0, 1),
+    dO = 3, with s chosen so that P_1 = 6.28e-6 lies between two fp16 subnormals
+    (spacing 2^-24). dV_1 = 3 P_1 (itself subnormal); an implementation that rounds
+    P_1 to fp16 as the product operand and the product to fp16 is off by about 1.2
+    spacings, 0.4% of dV_1: beyond half an ulp of the result plus 2 u M with the
+    relative roundoff u = 2^-11 alone, within 2 (u M + eta F)."""
+    p1 = 105.4 * 2.0 ** -24
+    s = math.log(p1 / (1.0 - p1))
+    q = np.ones((1, 1, 1, 1))
+    k = np.array([0.0, s]).reshape(1, 2, 1, 1)
+    v = np.array([0.0, 1.0]).reshape(1, 2, 1, 1)
+    do = np.full((1, 1, 1, 1), 3.0)
+    ref = oracle.backward(q, k, v, do, scale=1.0)
+    mag = oracle.backward_magnitudes(q, k, v, do, scale=1.0)
+    flo = oracle.backward_operand_sums(q, k, do, scale=1.0)
+    np.testing.assert_allclose(ref[2][0, 1, 0, 0], 3.0 * p1, rtol=1e-12)
+    np.testing.assert_allclose(flo[2][0, 1, 0, 0], 3.0, rtol=0)
+    got = ref[2].copy()
+    got[0, 1, 0, 0] = float(np.float16(float(np.float16(p1)) * 3.0))
+    assert abs(got[0, 1, 0, 0] - 3.0 * p1) > 2.0 ** -24
+    with pytest.raises(AssertionError):
+        cmp.check_grad(got, ref[2], mag[2], "f16", "dv without the absolute term")
+    assert cmp.check_grad(got, ref[2], mag[2], "f16", "dv", floor=flo[2]) <= 1.0

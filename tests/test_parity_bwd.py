@@ -54,9 +54,10 @@ def run_full(wid, B, Nq, Nk, Hq, Hkv, d, dtype, causal, scale=None, fwd="gpu", w
     dq, dk, dv = attention_backward(qd, kd, vd, o, lse, dod, causal=causal, scale=scale, window=window)
     ref = oracle.backward(q, k, v, do, causal=causal, scale=scale, window=window)
     mag = oracle.backward_magnitudes(q, k, v, do, causal=causal, scale=scale, window=window)
+    flo = oracle.backward_operand_sums(q, k, do, causal=causal, scale=scale, window=window)
     got = [to_np(g) for g in (dq, dk, dv)]
-    worst = [cmp.check_grad(g, r, m, dtype, f"{what} {n}")
-             for g, r, m, n in zip(got, ref, mag, ("dq", "dk", "dv"))]
+    worst = [cmp.check_grad(g, r, m, dtype, f"{what} {n}", floor=f)
+             for g, r, m, f, n in zip(got, ref, mag, flo, ("dq", "dk", "dv"))]
     # the pages' criterion: at most twice the error of a plain float32 implementation
     base = cmp.emulate_backward(q, k, v, do, causal, scale, dtype, window=window)
     errs = [cmp.check_grad_vs_baseline(g, r, e, dtype, f"{what} {n} vs float32 baseline")
@@ -203,10 +204,11 @@ element-wise bound and the pages' twice-the-baseline rule."""
         args = [oracle.widen(x[sl], w.dtype) for x in (q, k, v, do)]
         ref = oracle.backward(*args, causal=w.causal, scale=w.scale)
         mag = oracle.backward_magnitudes(*args, causal=w.causal, scale=w.scale)
+        flo = oracle.backward_operand_sums(args[0], args[1], args[3], causal=w.causal, scale=w.scale)
         base = cmp.emulate_backward(*args, w.causal, w.scale, w.dtype)
-        for g, r, m, e, n in zip((dq, dk, dv), ref, mag, base, ("dq", "dk", "dv")):
+        for g, r, m, f, e, n in zip((dq, dk, dv), ref, mag, flo, base, ("dq", "dk", "dv")):
             got = to_np(g[sl])
-            worst = cmp.check_grad(got, r, m, w.dtype, f"{w.name} b={b} h={h} {n}")
+            worst = cmp.check_grad(got, r, m, w.dtype, f"{w.name} b={b} h={h} {n}", floor=f)
             eg, eb = cmp.check_grad_vs_baseline(got, r, e, w.dtype, f"{w.name} b={b} h={h} {n} vs float32 baseline")
             print(f"[bwd] {w.name} b={b} h={h} {n}: ratio {worst:.3g}, max error {eg:.3g} (baseline {eb:.3g})",
                   flush=True)

@@ -59,9 +59,11 @@ def run(wid, lq, lk, Hq, Hkv, d, dtype, causal=False):
                 ((qb, q0, q1), (kb, k0, k1), (vb, k0, k1), (dob, q0, q1))]
         ref = oracle.backward(*args, causal=causal, scale=scale)
         mag = oracle.backward_magnitudes(*args, causal=causal, scale=scale)
-        for g, r, m, n in zip((dq[None, q0:q1], dk[None, k0:k1], dv[None, k0:k1]), ref, mag, ("dq", "dk", "dv")):
+        flo = oracle.backward_operand_sums(args[0], args[1], args[3], causal=causal, scale=scale)
+        for g, r, m, f, n in zip((dq[None, q0:q1], dk[None, k0:k1], dv[None, k0:k1]), ref, mag, flo,
+                                 ("dq", "dk", "dv")):
             if g.size:
-                worst = max(worst, cmp.check_grad(g, r, m, dtype, f"{what} {n}"))
+                worst = max(worst, cmp.check_grad(g, r, m, dtype, f"{what} {n}", floor=f))
     for b in range(len(lq)):
         if cq[b + 1] == cq[b]:   # keys no query sees have zero gradients
             assert np.all(dk[ck[b]:ck[b + 1]] == 0) and np.all(dv[ck[b]:ck[b + 1]] == 0)

@@ -61,8 +61,9 @@ def test_forward_and_backward_at_the_widest_rows(bits, dev, causal):
     cmp.check_lse(to_np(lse[:, hs]), lse_ref, what)
     ref = oracle.backward(q, k, v, do, causal=causal, scale=scale)
     mag = oracle.backward_magnitudes(q, k, v, do, causal=causal, scale=scale)
-    for g, r, m, n in zip((dq, dk, dv), ref, mag, ("dq", "dk", "dv")):
-        cmp.check_grad(to_np(g[:, :, hs]), r, m, DTYPE, f"{what} {n}")
+    flo = oracle.backward_operand_sums(q, k, do, causal=causal, scale=scale)
+    for g, r, m, f, n in zip((dq, dk, dv), ref, mag, flo, ("dq", "dk", "dv")):
+        cmp.check_grad(to_np(g[:, :, hs]), r, m, DTYPE, f"{what} {n}", floor=f)
 
 
 def test_decode_at_the_widest_rows(bits, dev):
@@ -133,8 +134,9 @@ def test_forward_and_backward_beyond_4_gib():
             if grads is not None:
                 ref = oracle.backward(qb, kb, vb, dob, causal=True, scale=scale)
                 mag = oracle.backward_magnitudes(qb, kb, vb, dob, causal=True, scale=scale)
-                for g, r, m, name in zip(grads, ref, mag, ("dq", "dk", "dv")):
-                    cmp.check_grad(to_np(g[b:b + 1]), r, m, dtype, f"{what} {name}")
+                flo = oracle.backward_operand_sums(qb, kb, dob, causal=True, scale=scale)
+                for g, r, m, f, name in zip(grads, ref, mag, flo, ("dq", "dk", "dv")):
+                    cmp.check_grad(to_np(g[b:b + 1]), r, m, dtype, f"{what} {name}", floor=f)
         del o, lse, grads
     del q, k, v, do
     torch.cuda.empty_cache()
