@@ -5,7 +5,8 @@ every head dim, fully masked rows). This one draws the shape, head grouping,
 head dim, dtype, mask, scale, for decode the split count and paging, and for
 packed batches the number of sequences and their query and key lengths (empty
 ones included) from a fixed seed, so that combinations nobody listed are
-covered too. Sizes stay small enough for the oracle to finish in well under a
+covered too; a few long single sequences (2048 to 4800 rows) reach the wide
+forward shape. Sizes stay small enough for the oracle to finish in about a
 second per case.
 """
 import math
@@ -119,6 +120,24 @@ FVL = _varlen_cases(_n(24), 6300, 300)
 BVL = _varlen_cases(_n(16), 6400, 200)
 
 
+def _long_cases(n):
+    # long single sequences (the 256-row workgroups of fp16 d = 128 without a
+    # band start at 3072 query rows), a few heads so the oracle stays quick
+    out = []
+    for i in range(n):
+        hkv = int(_rng.choice([1, 2]))
+        hq = hkv * int(_rng.choice([1, 2]))
+        nq, nk = int(_rng.integers(2048, 4800)), int(_rng.integers(1, 4800))
+        d = int(_rng.choice([64, 128, 128]))
+        dtype = str(_rng.choice(["f16", "f16", "bf16"]))
+        causal, window = _mask(nq, nk)
+        out.append((6500 + i, 1, nq, nk, hq, hkv, d, dtype, causal, window, _scale(d)))
+    return out
+
+
+LONG = _long_cases(_n(6))
+
+
 def _id(c):
     return "-".join(str(x) for x in c[1:])
 
@@ -168,3 +187,8 @@ def test_forward_varlen(case):
 def test_backward_varlen(case):
     wid, lq, lk, hq, hkv, d, dtype, causal = case
     bvl.run(wid, lq, lk, hq, hkv, d, dtype, causal=causal)
+
+
+@pytest.mark.parametrize("case", LONG, ids=_id)
+def test_forward_long(case):
+    test_forward(case)
