@@ -296,19 +296,21 @@ template <int D, bool BF16, bool BAND, bool WIDE = false> struct FwdWave {
     }
   }
 
+  // scores of keys this lane's row does not see -> -inf (tile jt)
+  __device__ __forceinline__ void mask(SA& sacc, int jt) const {
+    const int k0 = jt * C::BC;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key < lo_key || key > hi_key) sacc[kb][r] = kNegInf;
+      }
+  }
   // mask (if asked) and row max of the raw scores of tile jt
   template <bool MASK>
   __device__ __forceinline__ float rowmax(SA& sacc, int jt) const {
-    if (MASK) {
-      const int k0 = jt * C::BC;
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key < lo_key || key > hi_key) sacc[kb][r] = kNegInf;
-        }
-    }
+    if (MASK) mask(sacc, jt);
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
@@ -438,8 +440,22 @@ template <int D, bool BF16, bool BAND, bool WIDE = false> struct FwdWave {
         SA sacc;
         PF pf;
         qk(lds.k[ST], sacc);
-        rebase(rowmax<true>(sacc, j));
-        add_sum(probs<true>(sacc, pf));
+        if constexpr (D > 192) {
+          // the unmasked tiles' scheme on the masked scores: no row max unless a
+          // sum passes the cap or the reference is not set yet (fewer registers
+          // live at once: the d = 256 kernels spill less)
+          mask(sacc, j);
+          float ps = probs<true>(sacc, pf);
+          const bool need = !(ps <= kSumCap) || m_run == kNegInf;
+          if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+            rebase(rowmax<false>(sacc, j));
+            ps = probs<true>(sacc, pf);
+          }
+          add_sum(ps);
+        } else {
+          rebase(rowmax<true>(sacc, j));
+          add_sum(probs<true>(sacc, pf));
+        }
         pv(lds.v[ST], pf);
         if (BF16) l_part += rounded_sum(pf);
       }
