@@ -54,6 +54,9 @@ EDGE = [
     (1, 513, 1, 2, 1, 128, "bf16", False),
     (1, 256, 1000, 8, 8, 128, "f16", False),
     (3, 250, 250, 6, 6, 96, "bf16", False),
+    (1, 3, 65537, 2, 1, 128, "f16", False),   # a few rows over 65537 keys (2049 tiles, ragged tail)
+    (1, 3, 65537, 2, 1, 128, "bf16", True),
+    (1, 70001, 3, 2, 2, 128, "f16", False),   # 70001 rows (the 256-row shape) over 3 keys
 ]
 
 
