@@ -80,6 +80,8 @@ EDGE = [
     (1, 256, 1000, 8, 8, 128, "f16", False),
     (3, 250, 250, 6, 6, 96, "bf16", False),
     (1, 160, 160, 8, 1, 64, "bf16", True),    # one KV head for 8 query heads
+    (1, 3, 20001, 2, 1, 128, "bf16", False),  # a few rows over 20001 keys (157 key blocks)
+    (1, 20001, 5, 2, 2, 128, "f16", True),    # 20001 rows over 5 keys: almost all rows see them all
 ]
 
 

@@ -52,7 +52,7 @@ def test_split_count_invariance(splits):
     run(w.wid, 2, 1, 2048, w.Hq, w.Hkv, w.d, w.dtype, splits)
 
 
-@pytest.mark.parametrize("Nk,splits", [(1000, 16), (8191, 16), (33, 16), (1, 1), (31, 4), (100, 3)])
+@pytest.mark.parametrize("Nk,splits", [(1000, 16), (8191, 16), (33, 16), (1, 1), (31, 4), (100, 3), (300001, 64)])
 def test_ragged_cache_lengths(Nk, splits):
     run(500 + Nk % 97, 2, 1, Nk, 8, 2, 128, "bf16", splits)
 
