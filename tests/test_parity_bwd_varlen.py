@@ -82,6 +82,14 @@ def test_queries_and_keys_differ_per_sequence(causal):
     run(3600 + causal, [50, 200, 7, 64], [300, 10, 0, 64], 8, 8, 64, "f16", causal)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_short_sequences(causal):
+    # 600 sequences of 0 to 24 rows (seeded): the grid is mostly workgroups past
+    # their sequence's end, which must exit cleanly
+    lens = [int(x) for x in np.random.default_rng(3650).integers(0, 25, size=600)]
+    run(3650 + causal, lens, lens, 4, 2, 64, "bf16", causal)
+
+
 @pytest.mark.parametrize("d", [32, 64, 96, 128, 192, 256])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_head_dims(d, dtype):
