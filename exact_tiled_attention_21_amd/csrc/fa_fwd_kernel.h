@@ -26,11 +26,12 @@
 //
 // The reference max m used in P = exp2(s * scale * log2(e) - m) need not be
 // the running max: O and the row sum share it, so the result is the same for
-// any m as long as P stays in range. Masked tiles and the first unmasked tile
-// take the tile's row max and move m when it grows by more than 2^kLazy.
-// Unmasked tiles skip the row max altogether: they form P against the current
-// m and take the (rare) max-and-rebase path only when some lane's sum of the
-// tile's probabilities exceeds kSumCap, which bounds every P of the tile.
+// any m as long as P stays in range. Masked tiles take the tile's row max and
+// move m when it grows by more than 2^kLazy (at d = 256 they follow the
+// unmasked scheme below, which needs fewer registers). Unmasked tiles skip the
+// row max altogether: they form P against the current m and take the (rare)
+// max-and-rebase path only when some lane's sum of the tile's probabilities
+// exceeds kSumCap, which bounds every P of the tile, or when m is not set yet.
 #pragma once
 
 #include "fa_device.h"
